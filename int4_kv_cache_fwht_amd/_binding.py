@@ -1,0 +1,273 @@
+"""ctypes binding of libkv4 (names follow ``include/kv4.h``); argument marshalling only."""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass, asdict
+from typing import Optional, Sequence
+
+import torch  # loaded first so that libkv4 binds to the same HIP runtime as torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libkv4.so")
+
+FORMAT_INT4_PROT = 0
+FORMAT_INT8 = 1
+FORMAT_BF16 = 2
+
+STATUS = {
+    0: "KV4_OK",
+    1: "KV4_ERR_INVALID_ARGUMENT",
+    2: "KV4_ERR_OUT_OF_PAGES",
+    3: "KV4_ERR_SEQ_STATE",
+    4: "KV4_ERR_WORKSPACE_TOO_SMALL",
+    5: "KV4_ERR_UNSUPPORTED",
+    6: "KV4_ERR_HIP",
+}
+
+
+class KV4Error(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        self.name = STATUS.get(status, "KV4_UNKNOWN")
+        super().__init__("%s: %s" % (self.name, detail))
+
+
+class _Config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "num_q_heads", "num_kv_heads", "head_dim", "page_size", "num_pages", "max_seqs", "max_pages_per_seq",
+        "num_sinks", "num_recent", "hadamard_block", "format")]
+
+
+class _BufferSizes(ctypes.Structure):
+    _fields_ = [("page_pool", ctypes.c_size_t), ("int8_pool", ctypes.c_size_t), ("block_table", ctypes.c_size_t),
+                ("page_block_bytes", ctypes.c_size_t), ("int8_tile_bytes", ctypes.c_size_t),
+                ("int8_tiles", ctypes.c_int32)]
+
+
+class _Buffers(ctypes.Structure):
+    _fields_ = [("page_pool", ctypes.c_void_p), ("int8_pool", ctypes.c_void_p), ("block_table", ctypes.c_void_p)]
+
+
+@dataclass
+class Config:
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    num_pages: int
+    max_seqs: int
+    max_pages_per_seq: int
+    num_sinks: int = 4
+    num_recent: int = 128
+    hadamard_block: int = 128
+    format: int = FORMAT_INT4_PROT
+    page_size: int = 16
+
+    def to_c(self) -> _Config:
+        c = _Config()
+        for k, v in asdict(self).items():
+            setattr(c, k, int(v))
+        return c
+
+
+@dataclass
+class BufferSizes:
+    page_pool: int
+    int8_pool: int
+    block_table: int
+    page_block_bytes: int
+    int8_tile_bytes: int
+    int8_tiles: int
+
+
+_lib = None
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """Loads libkv4.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError("libkv4.so is not built (run __graft_entry__.build() or "
+                              "python -m int4_kv_cache_fwht_amd.build)")
+        L = ctypes.CDLL(_LIB_PATH)
+        P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        L.kv4_buffer_sizes_query.argtypes = [P, P]
+        L.kv4_cache_create.argtypes = [P, P, P]
+        L.kv4_cache_destroy.argtypes = [P]
+        L.kv4_append_workspace_size.argtypes = [P, I32, P, P, P]
+        L.kv4_append.argtypes = [P, I32, P, P, P, P, P, SZ, P]
+        L.kv4_seq_free.argtypes = [P, I32]
+        L.kv4_decode_workspace_size.argtypes = [P, I32, P]
+        L.kv4_decode_attention.argtypes = [P, I32, P, P, ctypes.c_float, P, P, SZ, P]
+        L.kv4_seq_length.argtypes = [P, I32, P]
+        L.kv4_block_table.argtypes = [P, I32, P, I32, P]
+        L.kv4_free_pages.argtypes = [P, P]
+        L.kv4_set_decode_waves.argtypes = [P, I32]
+        L.kv4_status_string.argtypes = [ctypes.c_int]
+        L.kv4_status_string.restype = ctypes.c_char_p
+        L.kv4_last_error.argtypes = [P]
+        L.kv4_last_error.restype = ctypes.c_char_p
+        for name in ("kv4_buffer_sizes_query", "kv4_cache_create", "kv4_cache_destroy", "kv4_append_workspace_size",
+                     "kv4_append", "kv4_seq_free", "kv4_decode_workspace_size", "kv4_decode_attention",
+                     "kv4_seq_length", "kv4_block_table", "kv4_free_pages", "kv4_set_decode_waves"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status: int, handle=None):
+    if status != 0:
+        detail = lib().kv4_last_error(handle)
+        raise KV4Error(status, detail.decode() if detail else "")
+
+
+def _i32_array(values: Sequence[int]):
+    arr = (ctypes.c_int32 * len(values))(*[int(v) for v in values])
+    return arr
+
+
+def kv4_buffer_sizes_query(cfg: Config) -> BufferSizes:
+    c = cfg.to_c()
+    out = _BufferSizes()
+    _check(lib().kv4_buffer_sizes_query(ctypes.byref(c), ctypes.byref(out)))
+    return BufferSizes(out.page_pool, out.int8_pool, out.block_table, out.page_block_bytes, out.int8_tile_bytes,
+                       out.int8_tiles)
+
+
+def _stream_ptr(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+class Cache:
+    """A kv4 cache over torch-allocated device buffers on ``device``.
+
+    Workspaces are cached per instance and grown on demand; calls through one instance must be
+    ordered on one stream (the library's own rule for a handle).
+    """
+
+    def __init__(self, cfg: Config, device="cuda"):
+        self.cfg = cfg
+        device = torch.device(device)
+        if device.type == "cuda" and device.index is None:
+            device = torch.device("cuda", torch.cuda.current_device())
+        self.device = device
+        self.sizes = kv4_buffer_sizes_query(cfg)
+        with torch.cuda.device(self.device):
+            self.page_pool = torch.empty(max(self.sizes.page_pool, 256), dtype=torch.uint8, device=self.device)
+            self.int8_pool = (torch.empty(self.sizes.int8_pool, dtype=torch.uint8, device=self.device)
+                              if self.sizes.int8_pool else None)
+            self.block_table_dev = torch.full((cfg.max_seqs, cfg.max_pages_per_seq), -1, dtype=torch.int32,
+                                              device=self.device)
+            bufs = _Buffers(self.page_pool.data_ptr(), self.int8_pool.data_ptr() if self.int8_pool is not None else None,
+                            self.block_table_dev.data_ptr())
+            c = cfg.to_c()
+            h = ctypes.c_void_p()
+            _check(lib().kv4_cache_create(ctypes.byref(c), ctypes.byref(bufs), ctypes.byref(h)))
+        self._h = h
+        self._ws_append = None
+        self._ws_decode = None
+
+    # -- lifetime --------------------------------------------------------------------------------
+    def close(self):
+        if getattr(self, "_h", None):
+            lib().kv4_cache_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def handle(self):
+        return self._h
+
+    # -- workspace -------------------------------------------------------------------------------
+    def _workspace(self, attr: str, nbytes: int) -> torch.Tensor:
+        ws = getattr(self, attr)
+        if ws is None or ws.numel() < nbytes:
+            ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+            setattr(self, attr, ws)
+        return ws
+
+    def append_workspace_size(self, seq_ids: Sequence[int], n_new: Sequence[int]) -> int:
+        ids, nn = _i32_array(seq_ids), _i32_array(n_new)
+        out = ctypes.c_size_t()
+        _check(lib().kv4_append_workspace_size(self._h, len(ids), ids, nn, ctypes.byref(out)), self._h)
+        return out.value
+
+    def decode_workspace_size(self, n_seqs: int) -> int:
+        out = ctypes.c_size_t()
+        _check(lib().kv4_decode_workspace_size(self._h, int(n_seqs), ctypes.byref(out)), self._h)
+        return out.value
+
+    # -- calls -------------------------------------------------------------------------------------
+    def append(self, seq_ids: Sequence[int], n_new: Sequence[int], k: Optional[torch.Tensor],
+               v: Optional[torch.Tensor], stream=None, workspace: Optional[torch.Tensor] = None):
+        """k, v: bf16 [sum(n_new), Hkv, D] on the cache's device (rows in call order)."""
+        ids, nn = _i32_array(seq_ids), _i32_array(n_new)
+        rows = sum(int(x) for x in n_new)
+        kp = vp = None
+        if rows > 0:
+            for t in (k, v):
+                if t is None or t.dtype != torch.bfloat16 or not t.is_contiguous() or t.device != self.device:
+                    raise ValueError("k / v must be contiguous bf16 tensors on the cache device")
+                if tuple(t.shape) != (rows, self.cfg.num_kv_heads, self.cfg.head_dim):
+                    raise ValueError("k / v shape must be [sum(n_new), Hkv, D]")
+            kp, vp = k.data_ptr(), v.data_ptr()
+        if workspace is None:
+            workspace = self._workspace("_ws_append", self.append_workspace_size(seq_ids, n_new))
+        st = _stream_ptr(stream)
+        _check(lib().kv4_append(self._h, len(ids), ids, nn, kp, vp, workspace.data_ptr(), workspace.numel(), st),
+               self._h)
+
+    def decode_attention(self, seq_ids: Sequence[int], q: torch.Tensor, scale: float = 0.0,
+                         out: Optional[torch.Tensor] = None, stream=None,
+                         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """q: bf16 [n, Hq, D] -> fp32 [n, Hq, D]."""
+        ids = _i32_array(seq_ids)
+        n = len(ids)
+        shape = (n, self.cfg.num_q_heads, self.cfg.head_dim)
+        if q.dtype != torch.bfloat16 or not q.is_contiguous() or tuple(q.shape) != shape or q.device != self.device:
+            raise ValueError("q must be a contiguous bf16 [n, Hq, D] tensor on the cache device")
+        if out is None:
+            out = torch.empty(shape, dtype=torch.float32, device=self.device)
+        elif out.dtype != torch.float32 or not out.is_contiguous() or tuple(out.shape) != shape:
+            raise ValueError("out must be a contiguous fp32 [n, Hq, D] tensor")
+        if workspace is None:
+            workspace = self._workspace("_ws_decode", self.decode_workspace_size(n))
+        st = _stream_ptr(stream)
+        _check(lib().kv4_decode_attention(self._h, n, ids, q.data_ptr(), float(scale), out.data_ptr(),
+                                          workspace.data_ptr(), workspace.numel(), st), self._h)
+        return out
+
+    def seq_free(self, seq_id: int):
+        _check(lib().kv4_seq_free(self._h, int(seq_id)), self._h)
+
+    def seq_length(self, seq_id: int) -> int:
+        out = ctypes.c_int32()
+        _check(lib().kv4_seq_length(self._h, int(seq_id), ctypes.byref(out)), self._h)
+        return out.value
+
+    def block_table(self, seq_id: int):
+        cap = self.cfg.max_pages_per_seq
+        buf = (ctypes.c_int32 * cap)()
+        n = ctypes.c_int32()
+        _check(lib().kv4_block_table(self._h, int(seq_id), buf, cap, ctypes.byref(n)), self._h)
+        return [buf[i] for i in range(min(n.value, cap))]
+
+    def free_pages(self) -> int:
+        out = ctypes.c_int32()
+        _check(lib().kv4_free_pages(self._h, ctypes.byref(out)), self._h)
+        return out.value
+
+    def set_decode_waves(self, waves: int):
+        _check(lib().kv4_set_decode_waves(self._h, int(waves)), self._h)

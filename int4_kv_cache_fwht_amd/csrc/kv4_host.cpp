@@ -1,0 +1,442 @@
+// kv4_host.cpp -- C ABI of libkv4 (see include/kv4.h): argument validation, host state, staging of
+// the per-call plans to the device and kernel launches.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "kv4.h"
+#include "kv4_launch.h"
+#include "kv4_plan.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+// Pinned host staging for the plans that each call copies to the device.  A slot is reused only
+// after the copy that read it has completed (its event).
+struct Staging {
+    struct Slot {
+        void* host = nullptr;
+        size_t cap = 0;
+        hipEvent_t ev = nullptr;
+        bool pending = false;
+    };
+    std::vector<Slot> slots;
+    int next = 0;
+
+    hipError_t init(int n)
+    {
+        slots.resize((size_t)n);
+        for (auto& s : slots) {
+            hipError_t e = hipEventCreateWithFlags(&s.ev, hipEventDisableTiming);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
+    void release()
+    {
+        for (auto& s : slots) {
+            if (s.pending) hipEventSynchronize(s.ev);
+            if (s.host) hipHostFree(s.host);
+            if (s.ev) hipEventDestroy(s.ev);
+            s = Slot();
+        }
+    }
+    hipError_t acquire(size_t bytes, void** host, int* idx)
+    {
+        Slot& s = slots[(size_t)next];
+        hipError_t e = hipSuccess;
+        if (s.pending) {
+            e = hipEventSynchronize(s.ev);
+            if (e != hipSuccess) return e;
+            s.pending = false;
+        }
+        if (s.cap < bytes) {
+            if (s.host) hipHostFree(s.host);
+            s.host = nullptr;
+            s.cap = 0;
+            size_t cap = bytes < 4096 ? 4096 : bytes;
+            e = hipHostMalloc(&s.host, cap, hipHostMallocDefault);
+            if (e != hipSuccess) return e;
+            s.cap = cap;
+        }
+        *host = s.host;
+        *idx = next;
+        next = (next + 1) % (int)slots.size();
+        return hipSuccess;
+    }
+    hipError_t commit(int idx, hipStream_t stream)
+    {
+        Slot& s = slots[(size_t)idx];
+        hipError_t e = hipEventRecord(s.ev, stream);
+        if (e == hipSuccess) s.pending = true;
+        return e;
+    }
+};
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+} // namespace
+
+struct kv4_cache {
+    kv4::State st;
+    kv4::Sizes sizes;
+    kv4_buffers bufs{};
+    int device = 0;
+    int num_cus = 256;
+    int decode_waves = 0; // 0: automatic
+    float cb = 1.0f;
+    Staging staging;
+    std::string err;
+};
+
+namespace {
+
+kv4_status fail(kv4_cache* h, kv4_status s, const std::string& msg)
+{
+    if (h)
+        h->err = msg;
+    else
+        g_last_error = msg;
+    return s;
+}
+
+kv4_status hip_fail(kv4_cache* h, hipError_t e, const char* where)
+{
+    std::string m = std::string(where) + ": " + hipGetErrorString(e);
+    return fail(h, KV4_ERR_HIP, m);
+}
+
+kv4::Config to_config(const kv4_config* c)
+{
+    kv4::Config k;
+    k.hq = c->num_q_heads;
+    k.hkv = c->num_kv_heads;
+    k.d = c->head_dim;
+    k.page = c->page_size;
+    k.num_pages = c->num_pages;
+    k.max_seqs = c->max_seqs;
+    k.max_pps = c->max_pages_per_seq;
+    k.sinks = c->num_sinks;
+    k.recent = c->num_recent;
+    k.block = c->hadamard_block;
+    k.format = c->format;
+    return k;
+}
+
+// RAII: make the cache's device current for the duration of a call.
+struct DeviceGuard {
+    int prev = -1;
+    bool changed = false;
+    hipError_t err = hipSuccess;
+    explicit DeviceGuard(int dev)
+    {
+        err = hipGetDevice(&prev);
+        if (err == hipSuccess && prev != dev) {
+            err = hipSetDevice(dev);
+            changed = (err == hipSuccess);
+        }
+    }
+    ~DeviceGuard()
+    {
+        if (changed) hipSetDevice(prev);
+    }
+};
+
+int auto_waves(const kv4_cache* h) { return h->num_cus * 8; }
+
+int max_waves(const kv4_cache* h)
+{
+    int w = auto_waves(h);
+    if (h->decode_waves > w) w = h->decode_waves;
+    return w;
+}
+
+size_t decode_ws_bytes(const kv4_cache* h, int64_t n_units, int64_t waves)
+{
+    const int G = h->st.cfg.hq / h->st.cfg.hkv;
+    const int D = h->st.cfg.d;
+    const int64_t parts = waves + n_units;
+    return align_up((size_t)n_units * sizeof(kv4::DecodeUnit)) + align_up((size_t)parts * G * 2 * sizeof(float)) +
+           align_up((size_t)parts * G * D * sizeof(float));
+}
+
+size_t append_task_bound(int32_t n_seqs, const int32_t* n_new)
+{
+    size_t tasks = 0;
+    for (int i = 0; i < n_seqs; i++)
+        if (n_new[i] > 0) tasks += (size_t)n_new[i] / kv4::kPageSize + 2;
+    return tasks;
+}
+
+} // namespace
+
+extern "C" {
+
+const char* kv4_status_string(kv4_status s)
+{
+    switch (s) {
+    case KV4_OK: return "KV4_OK";
+    case KV4_ERR_INVALID_ARGUMENT: return "KV4_ERR_INVALID_ARGUMENT";
+    case KV4_ERR_OUT_OF_PAGES: return "KV4_ERR_OUT_OF_PAGES";
+    case KV4_ERR_SEQ_STATE: return "KV4_ERR_SEQ_STATE";
+    case KV4_ERR_WORKSPACE_TOO_SMALL: return "KV4_ERR_WORKSPACE_TOO_SMALL";
+    case KV4_ERR_UNSUPPORTED: return "KV4_ERR_UNSUPPORTED";
+    case KV4_ERR_HIP: return "KV4_ERR_HIP";
+    }
+    return "KV4_UNKNOWN_STATUS";
+}
+
+const char* kv4_last_error(kv4_cache_t h) { return h ? h->err.c_str() : g_last_error.c_str(); }
+
+kv4_status kv4_buffer_sizes_query(const kv4_config* cfg, kv4_buffer_sizes* out)
+{
+    if (!cfg || !out) return fail(nullptr, KV4_ERR_INVALID_ARGUMENT, "null argument");
+    kv4::Config c = to_config(cfg);
+    std::string msg;
+    kv4::Status s = kv4::check_config(c, &msg);
+    if (s != kv4::OK) return fail(nullptr, (kv4_status)s, msg);
+    kv4::Sizes z = kv4::buffer_sizes(c);
+    out->page_pool = z.page_pool;
+    out->int8_pool = z.int8_pool;
+    out->block_table = z.block_table;
+    out->page_block_bytes = z.page_block;
+    out->int8_tile_bytes = z.int8_tile;
+    out->int8_tiles = z.int8_tiles;
+    return KV4_OK;
+}
+
+kv4_status kv4_cache_create(const kv4_config* cfg, const kv4_buffers* bufs, kv4_cache_t* out)
+{
+    if (!cfg || !bufs || !out) return fail(nullptr, KV4_ERR_INVALID_ARGUMENT, "null argument");
+    kv4::Config c = to_config(cfg);
+    std::string msg;
+    kv4::Status s = kv4::check_config(c, &msg);
+    if (s != kv4::OK) return fail(nullptr, (kv4_status)s, msg);
+    kv4::Sizes z = kv4::buffer_sizes(c);
+    if ((z.page_pool && !bufs->page_pool) || (z.int8_pool && !bufs->int8_pool) || !bufs->block_table)
+        return fail(nullptr, KV4_ERR_INVALID_ARGUMENT, "missing device buffer");
+    if (((uintptr_t)bufs->page_pool % kAlign) || ((uintptr_t)bufs->int8_pool % kAlign) ||
+        ((uintptr_t)bufs->block_table % 4))
+        return fail(nullptr, KV4_ERR_INVALID_ARGUMENT, "device buffers must be 256-byte aligned");
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(nullptr, e, "hipGetDevice");
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(nullptr, e, "hipDeviceGetAttribute");
+    kv4_cache* h = new (std::nothrow) kv4_cache();
+    if (!h) return fail(nullptr, KV4_ERR_INVALID_ARGUMENT, "out of host memory");
+    h->st.init(c);
+    h->sizes = z;
+    h->bufs = *bufs;
+    h->device = dev;
+    h->num_cus = cus > 0 ? cus : 256;
+    h->cb = (float)(1.0 / std::sqrt((double)c.block));
+    e = h->staging.init(8);
+    if (e != hipSuccess) {
+        h->staging.release();
+        delete h;
+        return hip_fail(nullptr, e, "hipEventCreate");
+    }
+    *out = h;
+    return KV4_OK;
+}
+
+kv4_status kv4_cache_destroy(kv4_cache_t h)
+{
+    if (!h) return fail(nullptr, KV4_ERR_INVALID_ARGUMENT, "null handle");
+    {
+        DeviceGuard g(h->device);
+        h->staging.release();
+    }
+    delete h;
+    return KV4_OK;
+}
+
+kv4_status kv4_append_workspace_size(kv4_cache_t h, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_new,
+                                     size_t* bytes)
+{
+    (void)seq_ids;
+    if (!h || !bytes || n_seqs < 0 || (n_seqs > 0 && !n_new)) return fail(h, KV4_ERR_INVALID_ARGUMENT, "bad argument");
+    for (int i = 0; i < n_seqs; i++)
+        if (n_new[i] < 0) return fail(h, KV4_ERR_INVALID_ARGUMENT, "n_new < 0");
+    *bytes = align_up(append_task_bound(n_seqs, n_new) * sizeof(kv4::AppendTask));
+    return KV4_OK;
+}
+
+kv4_status kv4_append(kv4_cache_t h, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_new, const void* k_new,
+                      const void* v_new, void* workspace, size_t ws_bytes, void* stream)
+{
+    if (!h) return fail(nullptr, KV4_ERR_INVALID_ARGUMENT, "null handle");
+    if (n_seqs < 0 || (n_seqs > 0 && (!seq_ids || !n_new))) return fail(h, KV4_ERR_INVALID_ARGUMENT, "bad argument list");
+    int64_t rows = 0;
+    for (int i = 0; i < n_seqs; i++) {
+        if (n_new[i] < 0) return fail(h, KV4_ERR_INVALID_ARGUMENT, "n_new < 0");
+        rows += n_new[i];
+    }
+    if (rows > 0 && (!k_new || !v_new)) return fail(h, KV4_ERR_INVALID_ARGUMENT, "null k_new / v_new");
+    const size_t need = align_up(append_task_bound(n_seqs, n_new) * sizeof(kv4::AppendTask));
+    if (rows > 0 && (!workspace || ws_bytes < need))
+        return fail(h, KV4_ERR_WORKSPACE_TOO_SMALL, "append workspace too small");
+    std::vector<kv4::AppendTask> tasks;
+    std::string msg;
+    kv4::Status s = h->st.plan_append(n_seqs, seq_ids, n_new, &tasks, &msg);
+    if (s != kv4::OK) return fail(h, (kv4_status)s, msg);
+    if (tasks.empty()) return KV4_OK;
+
+    DeviceGuard g(h->device);
+    if (g.err != hipSuccess) return hip_fail(h, g.err, "hipSetDevice");
+    hipStream_t strm = (hipStream_t)stream;
+    const size_t bytes = tasks.size() * sizeof(kv4::AppendTask);
+    void* host = nullptr;
+    int slot = 0;
+    hipError_t e = h->staging.acquire(bytes, &host, &slot);
+    if (e != hipSuccess) return hip_fail(h, e, "staging");
+    std::memcpy(host, tasks.data(), bytes);
+    e = hipMemcpyAsync(workspace, host, bytes, hipMemcpyHostToDevice, strm);
+    if (e != hipSuccess) return hip_fail(h, e, "hipMemcpyAsync");
+    e = h->staging.commit(slot, strm);
+    if (e != hipSuccess) return hip_fail(h, e, "hipEventRecord");
+
+    kv4::AppendArgs a;
+    a.tasks = (const kv4::AppendTask*)workspace;
+    a.k = (const uint16_t*)k_new;
+    a.v = (const uint16_t*)v_new;
+    a.pool = (uint8_t*)h->bufs.page_pool;
+    a.int8_pool = (uint8_t*)h->bufs.int8_pool;
+    a.bt = h->bufs.block_table;
+    a.page_block = (int64_t)h->sizes.page_block;
+    a.int8_tile = (int64_t)h->sizes.int8_tile;
+    a.hkv = h->st.cfg.hkv;
+    a.block = h->st.cfg.block;
+    a.sinks = h->st.cfg.sinks;
+    a.recent = h->st.cfg.recent;
+    a.int8_tiles = h->sizes.int8_tiles;
+    a.cb = h->cb;
+    e = kv4::launch_append(h->st.cfg.d, h->st.cfg.format, (int)tasks.size(), a, strm);
+    if (e != hipSuccess) return hip_fail(h, e, "append launch");
+    return KV4_OK;
+}
+
+kv4_status kv4_seq_free(kv4_cache_t h, int32_t seq_id)
+{
+    if (!h) return fail(nullptr, KV4_ERR_INVALID_ARGUMENT, "null handle");
+    std::string msg;
+    kv4::Status s = h->st.seq_free(seq_id, &msg);
+    if (s != kv4::OK) return fail(h, (kv4_status)s, msg);
+    return KV4_OK;
+}
+
+kv4_status kv4_decode_workspace_size(kv4_cache_t h, int32_t n_seqs, size_t* bytes)
+{
+    if (!h || !bytes || n_seqs < 0) return fail(h, KV4_ERR_INVALID_ARGUMENT, "bad argument");
+    *bytes = decode_ws_bytes(h, (int64_t)n_seqs * h->st.cfg.hkv, max_waves(h));
+    return KV4_OK;
+}
+
+kv4_status kv4_decode_attention(kv4_cache_t h, int32_t n_seqs, const int32_t* seq_ids, const void* q, float scale,
+                                float* out, void* workspace, size_t ws_bytes, void* stream)
+{
+    if (!h) return fail(nullptr, KV4_ERR_INVALID_ARGUMENT, "null handle");
+    if (n_seqs < 0 || (n_seqs > 0 && (!seq_ids || !q || !out))) return fail(h, KV4_ERR_INVALID_ARGUMENT, "bad argument list");
+    if (!std::isfinite(scale)) return fail(h, KV4_ERR_INVALID_ARGUMENT, "scale must be finite");
+    std::vector<kv4::DecodeUnit> units;
+    int64_t total = 0;
+    std::string msg;
+    kv4::Status s = h->st.plan_decode(n_seqs, seq_ids, &units, &total, &msg);
+    if (s != kv4::OK) return fail(h, (kv4_status)s, msg);
+    if (units.empty()) return KV4_OK;
+    const int64_t wmax = max_waves(h);
+    int64_t W = h->decode_waves > 0 ? h->decode_waves : auto_waves(h);
+    if (W > total) W = total;
+    if (W < 1) W = 1;
+    const int64_t n_units = (int64_t)units.size();
+    if (!workspace || ws_bytes < decode_ws_bytes(h, n_units, W) || W > wmax)
+        return fail(h, KV4_ERR_WORKSPACE_TOO_SMALL, "decode workspace too small");
+
+    DeviceGuard g(h->device);
+    if (g.err != hipSuccess) return hip_fail(h, g.err, "hipSetDevice");
+    hipStream_t strm = (hipStream_t)stream;
+    const size_t ubytes = (size_t)n_units * sizeof(kv4::DecodeUnit);
+    void* host = nullptr;
+    int slot = 0;
+    hipError_t e = h->staging.acquire(ubytes, &host, &slot);
+    if (e != hipSuccess) return hip_fail(h, e, "staging");
+    std::memcpy(host, units.data(), ubytes);
+    e = hipMemcpyAsync(workspace, host, ubytes, hipMemcpyHostToDevice, strm);
+    if (e != hipSuccess) return hip_fail(h, e, "hipMemcpyAsync");
+    e = h->staging.commit(slot, strm);
+    if (e != hipSuccess) return hip_fail(h, e, "hipEventRecord");
+
+    const int G = h->st.cfg.hq / h->st.cfg.hkv;
+    const int D = h->st.cfg.d;
+    const int64_t parts = W + n_units;
+    uint8_t* ws = (uint8_t*)workspace;
+    kv4::DecodeArgs a;
+    a.pool = (const uint8_t*)h->bufs.page_pool;
+    a.int8_pool = (const uint8_t*)h->bufs.int8_pool;
+    a.bt = h->bufs.block_table;
+    a.q = (const uint16_t*)q;
+    a.units = (const kv4::DecodeUnit*)ws;
+    a.part_ml = (float*)(ws + align_up(ubytes));
+    a.part_o = (float*)(ws + align_up(ubytes) + align_up((size_t)parts * G * 2 * sizeof(float)));
+    a.out = out;
+    a.total_steps = total;
+    a.page_block = (int64_t)h->sizes.page_block;
+    a.int8_tile = (int64_t)h->sizes.int8_tile;
+    a.n_units = (int)n_units;
+    a.n_waves = (int)W;
+    a.hkv = h->st.cfg.hkv;
+    a.max_pps = h->st.cfg.max_pps;
+    a.sinks = h->st.cfg.sinks;
+    a.recent = h->st.cfg.recent;
+    a.block = h->st.cfg.block;
+    a.int8_tiles = h->sizes.int8_tiles;
+    a.cb = h->cb;
+    const double sc = scale > 0.f ? (double)scale : 1.0 / std::sqrt((double)D);
+    a.scale_log2 = (float)(sc * 1.4426950408889634);
+    e = kv4::launch_decode(D, G, h->st.cfg.format, a, strm);
+    if (e != hipSuccess) return hip_fail(h, e, "decode launch");
+    return KV4_OK;
+}
+
+kv4_status kv4_seq_length(kv4_cache_t h, int32_t seq_id, int32_t* len)
+{
+    if (!h || !len) return fail(h, KV4_ERR_INVALID_ARGUMENT, "null argument");
+    if (seq_id < 0 || seq_id >= h->st.cfg.max_seqs) return fail(h, KV4_ERR_INVALID_ARGUMENT, "sequence id out of range");
+    *len = h->st.len[(size_t)seq_id];
+    return KV4_OK;
+}
+
+kv4_status kv4_block_table(kv4_cache_t h, int32_t seq_id, int32_t* pages, int32_t cap, int32_t* n)
+{
+    if (!h || !n || cap < 0 || (cap > 0 && !pages)) return fail(h, KV4_ERR_INVALID_ARGUMENT, "bad argument");
+    if (seq_id < 0 || seq_id >= h->st.cfg.max_seqs) return fail(h, KV4_ERR_INVALID_ARGUMENT, "sequence id out of range");
+    const int np = (h->st.len[(size_t)seq_id] + kv4::kPageSize - 1) / kv4::kPageSize;
+    for (int j = 0; j < np && j < cap; j++) pages[j] = h->st.bt[(size_t)seq_id * h->st.cfg.max_pps + j];
+    *n = np;
+    return KV4_OK;
+}
+
+kv4_status kv4_free_pages(kv4_cache_t h, int32_t* n)
+{
+    if (!h || !n) return fail(h, KV4_ERR_INVALID_ARGUMENT, "null argument");
+    *n = (int32_t)h->st.free_list.size();
+    return KV4_OK;
+}
+
+kv4_status kv4_set_decode_waves(kv4_cache_t h, int32_t waves)
+{
+    if (!h || waves < 0) return fail(h, KV4_ERR_INVALID_ARGUMENT, "bad argument");
+    h->decode_waves = waves;
+    return KV4_OK;
+}
+
+} // extern "C"

@@ -1,0 +1,45 @@
+// kv4_launch.h -- launch interface between the host library and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kv4_device_types.h"
+
+namespace kv4 {
+
+struct AppendArgs {
+    const AppendTask* tasks; // device copy of the call's tasks
+    const uint16_t* k;       // bf16 [rows][hkv][D]
+    const uint16_t* v;
+    uint8_t* pool;
+    uint8_t* int8_pool;
+    int32_t* bt;
+    int64_t page_block;
+    int64_t int8_tile;
+    int hkv, block, sinks, recent, int8_tiles;
+    float cb; // fl32(1/sqrt(block))
+};
+
+struct DecodeArgs {
+    const uint8_t* pool;
+    const uint8_t* int8_pool;
+    const int32_t* bt;
+    const uint16_t* q;        // bf16 [entries][hq][D]
+    const DecodeUnit* units;  // device copy of the plan
+    float* part_ml;           // [(W + n_units)][G][2] : (reference max in log2 units, sum)
+    float* part_o;            // [(W + n_units)][G][D]
+    float* out;               // fp32 [entries][hq][D]
+    int64_t total_steps;
+    int64_t page_block;
+    int64_t int8_tile;
+    int n_units, n_waves;
+    int hkv, max_pps, sinks, recent, block, int8_tiles;
+    float cb;         // fl32(1/sqrt(block))
+    float scale_log2; // softmax scale * log2(e)
+};
+
+hipError_t launch_append(int d, int format, int n_tasks, const AppendArgs& a, hipStream_t stream);
+hipError_t launch_decode(int d, int g, int format, const DecodeArgs& a, hipStream_t stream);
+
+} // namespace kv4
