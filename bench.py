@@ -1,0 +1,317 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the INT4 KV cache on one MI355X.
+
+One step = one pass of the hot path over one batch: append one new position to every sequence
+(fused rotation + quantization into the paged cache, INT8 protection of the newest positions)
+and then GQA decode attention over every sequence's full context.  The timed region holds
+exactly --steps steps, bracketed by device synchronization; inputs are resident in HBM.
+
+Prints ONE JSON line.  value = kv-tokens/s = (sum of context lengths attended per step) x steps /
+wall time.  roofline = the decode split-KV kernel's algorithmic bytes per launch / its average
+duration (HIP events recorded by the library on the call's stream), against the 8 TB/s HBM peak.
+cpu_baseline = the CPU oracle's decode on a bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+METRIC = "INT4-KV decode attention kv-tokens/s and achieved HBM GB/s (% of MI355X peak)"
+FORMATS = {"int4": 0, "int8": 1, "bf16": 2}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=4)
+    ap.add_argument("--workload", default="qwen3_8b_layer",
+                    choices=["qwen3_8b_layer", "rollout", "long_context", "tiny"])
+    ap.add_argument("--caches", type=int, default=4, help="distinct layer caches cycled (defeats the 256 MB MALL)")
+    ap.add_argument("--baselines", default="int8,bf16", help="comma list of baseline formats ('' for none)")
+    ap.add_argument("--baseline-steps", type=int, default=12)
+    ap.add_argument("--cpu-baseline-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-waves", type=int, default=0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (reference kernel for PMC byte counters)")
+    return ap.parse_args()
+
+
+def per_token_bytes(fmt, hkv, d):
+    """Algorithmic bytes per cached position (all kv heads, K and V)."""
+    if fmt == "int4":
+        return hkv * 2 * (d // 2 + 4)
+    if fmt == "int8":
+        return hkv * 2 * (d + 4)
+    return hkv * 2 * d * 2
+
+
+def decode_bytes(fmt, lens, w):
+    """Algorithmic HBM bytes of one decode launch: cached positions read once (INT4 pages for
+    unprotected positions, INT8 for the protected ones), block-table entries, q in, out out."""
+    hkv, d, hq = w.num_kv_heads, w.head_dim, w.num_q_heads
+    b4, b8 = per_token_bytes("int4", hkv, d), per_token_bytes("int8", hkv, d)
+    total = 0
+    for L in lens:
+        if fmt == "int4":
+            p = min(L, w.num_sinks + w.num_recent)
+            total += (L - p) * b4 + p * b8
+        else:
+            total += L * per_token_bytes(fmt, hkv, d)
+        total += math.ceil(L / 16) * 4 + hq * d * 2 + hq * d * 4
+    return total
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for name in ("kv4_kernels.hip", "kv4_launch.h", "kv4_device_types.h"):
+        with open(os.path.join(ROOT, "int4_kv_cache_fwht_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, fmt):
+    """Per-launch HBM bytes of the split kernel from committed rocprofv3 PMC runs, if they were taken
+    on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "decode_split_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = rec.get("%s/%s" % (workload, fmt))
+    if not e or e.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+class Bench:
+    def __init__(self, w, fmt, n_caches, total_steps, device, decode_waves):
+        import torch
+        import int4_kv_cache_fwht_amd as kv4
+        import kv4_inputs as W
+        self.torch, self.kv4, self.W = torch, kv4, W
+        self.w, self.fmt, self.device = w, fmt, device
+        self.lens0 = w.lengths()
+        B = w.batch
+        growth = math.ceil(total_steps / n_caches) + 1
+        max_len = max(self.lens0) + growth
+        pages = sum(math.ceil((L + growth) / 16) for L in self.lens0) + B
+        self.channels = W.outlier_channels(w.num_kv_heads, w.head_dim, w.outlier_channels, w.seed)
+        self.caches, self.lens = [], []
+        for c in range(n_caches):
+            cfg = kv4.Config(num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+                             num_pages=pages, max_seqs=B, max_pages_per_seq=math.ceil(max_len / 16) + 1,
+                             num_sinks=w.num_sinks, num_recent=w.num_recent,
+                             hadamard_block=w.hadamard_block if fmt != "bf16" else 1, format=FORMATS[fmt])
+            cache = kv4.Cache(cfg, device)
+            if decode_waves:
+                cache.set_decode_waves(decode_waves)
+            self._prefill(cache, layer=c)
+            self.caches.append(cache)
+            self.lens.append(list(self.lens0))
+        self.ids = list(range(B))
+        # per-step inputs, resident before timing
+        self.kn, self.vn, self.q = [], [], []
+        for s in range(total_steps):
+            k, v = W.seq_kv(w.num_kv_heads, w.head_dim, B, self.channels, w.outlier_scale, w.seed, 1000 + s, 0,
+                            device)
+            self.kn.append(k)
+            self.vn.append(v)
+            self.q.append(W.queries(B, w.num_q_heads, w.head_dim, w.seed, step=s, device=device))
+        self.out = torch.empty((B, w.num_q_heads, w.head_dim), dtype=torch.float32, device=device)
+        self.step_idx = 0
+        torch.cuda.synchronize()
+
+    def _prefill(self, cache, layer):
+        torch, W, w = self.torch, self.W, self.w
+        ids, chunk, rows = [], [], 0
+        for i, L in enumerate(self.lens0):
+            ids.append(i)
+            chunk.append(L)
+            rows += L
+            if rows >= 65536 or i == len(self.lens0) - 1:
+                ks, vs = [], []
+                for j, Lj in zip(ids, chunk):
+                    k, v = W.seq_kv(w.num_kv_heads, w.head_dim, Lj, self.channels, w.outlier_scale, w.seed, layer, j,
+                                    self.device)
+                    ks.append(k)
+                    vs.append(v)
+                cache.append(ids, chunk, torch.cat(ks).contiguous(), torch.cat(vs).contiguous())
+                ids, chunk, rows = [], [], 0
+        torch.cuda.synchronize()
+
+    def step(self):
+        """One step on the next cache; returns the kv-tokens attended."""
+        s = self.step_idx
+        c = s % len(self.caches)
+        cache = self.caches[c]
+        cache.append(self.ids, [1] * len(self.ids), self.kn[s], self.vn[s])
+        cache.decode_attention(self.ids, self.q[s], out=self.out)
+        self.lens[c] = [L + 1 for L in self.lens[c]]
+        self.step_idx += 1
+        return sum(self.lens[c]), self.lens[c]
+
+    def timed(self, steps):
+        torch = self.torch
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        toks = 0
+        for _ in range(steps):
+            toks += self.step()[0]
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, toks
+
+    def profiled(self, steps):
+        """Steps with the library's kernel events on; returns (split avg s, merge avg s, append avg s,
+        algorithmic bytes per split launch averaged)."""
+        for c in self.caches:
+            c.profile_enable(True)
+        nbytes = 0
+        for _ in range(steps):
+            _, lens = self.step()
+            nbytes += decode_bytes(self.fmt, lens, self.w)
+        tot = {"split_ms": 0.0, "merge_ms": 0.0, "append_ms": 0.0, "decode_launches": 0, "append_launches": 0}
+        for c in self.caches:
+            p = c.profile_read()
+            for k in tot:
+                tot[k] += p[k]
+            c.profile_enable(False)
+        n = max(tot["decode_launches"], 1)
+        return (tot["split_ms"] / n * 1e-3, tot["merge_ms"] / n * 1e-3,
+                tot["append_ms"] / max(tot["append_launches"], 1) * 1e-3, nbytes / n)
+
+
+def cpu_baseline(w, seconds, device):
+    """The oracle's decode (fp64, threaded) on a bounded sample of the workload: the first sequences
+    of layer 0, decoded repeatedly for about `seconds` of CPU time."""
+    import torch
+    import kv4_inputs as W
+    import oracle
+    lens = w.lengths()
+    n_s = min(len(lens), 4)
+    ids = list(range(n_s))
+    ch = W.outlier_channels(w.num_kv_heads, w.head_dim, w.outlier_channels, w.seed)
+    ora = oracle.OracleCache(w.num_q_heads, w.num_kv_heads, w.head_dim, 16,
+                             sum(math.ceil(L / 16) for L in lens[:n_s]) + 1, n_s,
+                             max(math.ceil(L / 16) for L in lens[:n_s]) + 1, w.num_sinks, w.num_recent,
+                             w.hadamard_block)
+    for i in ids:
+        k, v = W.seq_kv(w.num_kv_heads, w.head_dim, lens[i], ch, w.outlier_scale, w.seed, 0, i, device)
+        assert ora.append([i], [lens[i]], W.bf16_bits(k), W.bf16_bits(v)) == oracle.OK
+    q = W.bf16_bits(W.queries(n_s, w.num_q_heads, w.head_dim, w.seed, device=device))
+    threads = min(16, os.cpu_count() or 1)
+    reps, used, t0 = 0, 0, time.perf_counter()
+    while True:
+        _, used = ora.decode(ids, q, threads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 1000:
+            break
+    toks = reps * sum(lens[:n_s])
+    return {"value": toks / el, "unit": "kv-tokens/s", "cores": used, "kind": "oracle",
+            "sample": "%d sequences (%d positions) of %s, oracle decode in fp64 repeated %d times (%.1f s)" % (
+                n_s, sum(lens[:n_s]), w.name, reps, el)}
+
+
+def copy_probe(device):
+    """Plain device copy of 1 GiB (the reference kernel for PMC byte counters) -> GB/s moved."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device=device)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    reps = 5
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    del a, b
+    return 2 * n * reps / el / 1e9
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on exactly one GPU: the decode path is built and measured on one GPU "
+              "(multi-GPU sharding is not built); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import kv4_inputs as W
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    device = torch.device("cuda", 0)
+    w = W.WORKLOADS[args.workload]
+    total = args.warmup + args.steps + 12
+
+    print("bench: building %d int4 caches for %s" % (args.caches, w.name), file=sys.stderr, flush=True)
+    b = Bench(w, "int4", args.caches, total, device, args.decode_waves)
+    for _ in range(args.warmup):
+        b.step()
+    el, toks = b.timed(args.steps)
+    split_s, merge_s, append_s, bytes_per_launch = b.profiled(12)
+    achieved = bytes_per_launch / split_s / 1e9
+    traffic = measured_traffic(w.name, "int4")
+    kvtok_step = toks / args.steps
+    result = {
+        "metric": METRIC,
+        "value": toks / el,
+        "unit": "kv-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": el / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "kv_heads": w.num_kv_heads, "q_heads": w.num_q_heads,
+                   "head_dim": w.head_dim, "context": "%s%s" % (w.lengths_kind, list(w.length_args)),
+                   "sinks": w.num_sinks, "recent": w.num_recent, "hadamard_block": w.hadamard_block,
+                   "kv_storage": "int4 pages + int8 sink/recent", "distinct_caches": args.caches,
+                   "kv_tokens_per_step": kvtok_step},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "kernel": "decode_split_kernel<128,4,INT4_PROT>", "avg_launch_us": split_s * 1e6,
+                     "algorithmic_bytes_per_launch": bytes_per_launch},
+        "step_breakdown_us": {"append": append_s * 1e6, "decode_split": split_s * 1e6, "decode_merge": merge_s * 1e6},
+    }
+    del b
+    torch.cuda.empty_cache()
+
+    base = {}
+    for fmt in [f for f in args.baselines.split(",") if f]:
+        print("bench: baseline %s" % fmt, file=sys.stderr, flush=True)
+        bb = Bench(w, fmt, args.caches, args.warmup + 2 * args.baseline_steps, device, args.decode_waves)
+        for _ in range(args.warmup):
+            bb.step()
+        el2, toks2 = bb.timed(args.baseline_steps)
+        s2, m2, a2, by2 = bb.profiled(args.baseline_steps)
+        ach2 = by2 / s2 / 1e9
+        base[fmt] = {"kv_tokens_per_s": toks2 / el2, "ms_per_step": el2 / args.baseline_steps * 1e3,
+                     "split_avg_us": s2 * 1e6, "achieved_GBps": ach2, "frac": ach2 / HBM_PEAK_GBPS,
+                     "int4_speedup": (toks / el) / (toks2 / el2)}
+        del bb
+        torch.cuda.empty_cache()
+    if base:
+        result["baselines"] = base
+    if args.copy_calibration:
+        result["copy_probe_GBps"] = copy_probe(device)
+    if not args.no_cpu_baseline:
+        print("bench: cpu baseline", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_baseline_seconds, device)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

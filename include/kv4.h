@@ -180,6 +180,19 @@ kv4_status kv4_free_pages(kv4_cache_t h, int32_t* n);
 /* Tuning: number of waves the decode split kernel launches (0 = automatic). */
 kv4_status kv4_set_decode_waves(kv4_cache_t h, int32_t waves);
 
+/* Kernel timing (measurement of the hot path).  When enabled, every call records HIP events on
+ * its own stream around each kernel it launches; kv4_profile_read waits for them and returns the
+ * summed durations.  Enabling (or disabling) resets the totals.  Off by default. */
+typedef struct kv4_profile {
+    int64_t append_launches;
+    double append_ms;  /* append kernels */
+    int64_t decode_launches;
+    double split_ms;   /* decode split-KV kernels */
+    double merge_ms;   /* decode merge + inverse-rotation kernels */
+} kv4_profile;
+kv4_status kv4_profile_enable(kv4_cache_t h, int32_t enable);
+kv4_status kv4_profile_read(kv4_cache_t h, kv4_profile* out);
+
 const char* kv4_status_string(kv4_status s);
 /* Detail of the last error on h (or of the last handle-less error when h is NULL). */
 const char* kv4_last_error(kv4_cache_t h);

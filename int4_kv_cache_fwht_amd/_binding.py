@@ -45,6 +45,11 @@ class _BufferSizes(ctypes.Structure):
                 ("int8_tiles", ctypes.c_int32)]
 
 
+class _Profile(ctypes.Structure):
+    _fields_ = [("append_launches", ctypes.c_int64), ("append_ms", ctypes.c_double),
+                ("decode_launches", ctypes.c_int64), ("split_ms", ctypes.c_double), ("merge_ms", ctypes.c_double)]
+
+
 class _Buffers(ctypes.Structure):
     _fields_ = [("page_pool", ctypes.c_void_p), ("int8_pool", ctypes.c_void_p), ("block_table", ctypes.c_void_p)]
 
@@ -108,13 +113,16 @@ def lib():
         L.kv4_block_table.argtypes = [P, I32, P, I32, P]
         L.kv4_free_pages.argtypes = [P, P]
         L.kv4_set_decode_waves.argtypes = [P, I32]
+        L.kv4_profile_enable.argtypes = [P, I32]
+        L.kv4_profile_read.argtypes = [P, P]
         L.kv4_status_string.argtypes = [ctypes.c_int]
         L.kv4_status_string.restype = ctypes.c_char_p
         L.kv4_last_error.argtypes = [P]
         L.kv4_last_error.restype = ctypes.c_char_p
         for name in ("kv4_buffer_sizes_query", "kv4_cache_create", "kv4_cache_destroy", "kv4_append_workspace_size",
                      "kv4_append", "kv4_seq_free", "kv4_decode_workspace_size", "kv4_decode_attention",
-                     "kv4_seq_length", "kv4_block_table", "kv4_free_pages", "kv4_set_decode_waves"):
+                     "kv4_seq_length", "kv4_block_table", "kv4_free_pages", "kv4_set_decode_waves",
+                     "kv4_profile_enable", "kv4_profile_read"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -271,3 +279,12 @@ class Cache:
 
     def set_decode_waves(self, waves: int):
         _check(lib().kv4_set_decode_waves(self._h, int(waves)), self._h)
+
+    def profile_enable(self, enable: bool = True):
+        _check(lib().kv4_profile_enable(self._h, 1 if enable else 0), self._h)
+
+    def profile_read(self) -> dict:
+        p = _Profile()
+        _check(lib().kv4_profile_read(self._h, ctypes.byref(p)), self._h)
+        return {"append_launches": p.append_launches, "append_ms": p.append_ms,
+                "decode_launches": p.decode_launches, "split_ms": p.split_ms, "merge_ms": p.merge_ms}

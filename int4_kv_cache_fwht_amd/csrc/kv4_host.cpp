@@ -79,6 +79,62 @@ struct Staging {
     }
 };
 
+// Event pairs / triples recorded around kernel launches while profiling is on.
+struct Profiler {
+    bool on = false;
+    std::vector<std::vector<hipEvent_t>> append_ev; // {before, after}
+    std::vector<std::vector<hipEvent_t>> decode_ev; // {before split, after split, after merge}
+    kv4_profile totals{};
+
+    static hipError_t make(int n, std::vector<hipEvent_t>* out)
+    {
+        out->assign((size_t)n, nullptr);
+        for (auto& e : *out) {
+            hipError_t r = hipEventCreate(&e);
+            if (r != hipSuccess) return r;
+        }
+        return hipSuccess;
+    }
+    void reset()
+    {
+        for (auto& v : append_ev)
+            for (auto e : v)
+                if (e) hipEventDestroy(e);
+        for (auto& v : decode_ev)
+            for (auto e : v)
+                if (e) hipEventDestroy(e);
+        append_ev.clear();
+        decode_ev.clear();
+        totals = kv4_profile{};
+    }
+    hipError_t collect()
+    {
+        for (auto& v : append_ev) {
+            hipError_t r = hipEventSynchronize(v[1]);
+            if (r != hipSuccess) return r;
+            float ms = 0.f;
+            hipEventElapsedTime(&ms, v[0], v[1]);
+            totals.append_launches += 1;
+            totals.append_ms += ms;
+            for (auto e : v) hipEventDestroy(e);
+        }
+        append_ev.clear();
+        for (auto& v : decode_ev) {
+            hipError_t r = hipEventSynchronize(v[2]);
+            if (r != hipSuccess) return r;
+            float a = 0.f, b = 0.f;
+            hipEventElapsedTime(&a, v[0], v[1]);
+            hipEventElapsedTime(&b, v[1], v[2]);
+            totals.decode_launches += 1;
+            totals.split_ms += a;
+            totals.merge_ms += b;
+            for (auto e : v) hipEventDestroy(e);
+        }
+        decode_ev.clear();
+        return hipSuccess;
+    }
+};
+
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -93,6 +149,7 @@ struct kv4_cache {
     int decode_waves = 0; // 0: automatic
     float cb = 1.0f;
     Staging staging;
+    Profiler prof;
     std::string err;
 };
 
@@ -255,6 +312,7 @@ kv4_status kv4_cache_destroy(kv4_cache_t h)
     {
         DeviceGuard g(h->device);
         h->staging.release();
+        h->prof.reset();
     }
     delete h;
     return KV4_OK;
@@ -320,8 +378,19 @@ kv4_status kv4_append(kv4_cache_t h, int32_t n_seqs, const int32_t* seq_ids, con
     a.recent = h->st.cfg.recent;
     a.int8_tiles = h->sizes.int8_tiles;
     a.cb = h->cb;
+    std::vector<hipEvent_t> ev;
+    if (h->prof.on) {
+        e = Profiler::make(2, &ev);
+        if (e == hipSuccess) e = hipEventRecord(ev[0], strm);
+        if (e != hipSuccess) return hip_fail(h, e, "profiling event");
+    }
     e = kv4::launch_append(h->st.cfg.d, h->st.cfg.format, (int)tasks.size(), a, strm);
     if (e != hipSuccess) return hip_fail(h, e, "append launch");
+    if (h->prof.on) {
+        e = hipEventRecord(ev[1], strm);
+        if (e != hipSuccess) return hip_fail(h, e, "profiling event");
+        h->prof.append_ev.push_back(ev);
+    }
     return KV4_OK;
 }
 
@@ -402,8 +471,25 @@ kv4_status kv4_decode_attention(kv4_cache_t h, int32_t n_seqs, const int32_t* se
     a.cb = h->cb;
     const double sc = scale > 0.f ? (double)scale : 1.0 / std::sqrt((double)D);
     a.scale_log2 = (float)(sc * 1.4426950408889634);
-    e = kv4::launch_decode(D, G, h->st.cfg.format, a, strm);
-    if (e != hipSuccess) return hip_fail(h, e, "decode launch");
+    std::vector<hipEvent_t> ev;
+    if (h->prof.on) {
+        e = Profiler::make(3, &ev);
+        if (e == hipSuccess) e = hipEventRecord(ev[0], strm);
+        if (e != hipSuccess) return hip_fail(h, e, "profiling event");
+    }
+    e = kv4::launch_decode_split(D, G, h->st.cfg.format, a, strm);
+    if (e != hipSuccess) return hip_fail(h, e, "decode split launch");
+    if (h->prof.on) {
+        e = hipEventRecord(ev[1], strm);
+        if (e != hipSuccess) return hip_fail(h, e, "profiling event");
+    }
+    e = kv4::launch_decode_merge(D, G, h->st.cfg.format, a, strm);
+    if (e != hipSuccess) return hip_fail(h, e, "decode merge launch");
+    if (h->prof.on) {
+        e = hipEventRecord(ev[2], strm);
+        if (e != hipSuccess) return hip_fail(h, e, "profiling event");
+        h->prof.decode_ev.push_back(ev);
+    }
     return KV4_OK;
 }
 
@@ -436,6 +522,25 @@ kv4_status kv4_set_decode_waves(kv4_cache_t h, int32_t waves)
 {
     if (!h || waves < 0) return fail(h, KV4_ERR_INVALID_ARGUMENT, "bad argument");
     h->decode_waves = waves;
+    return KV4_OK;
+}
+
+kv4_status kv4_profile_enable(kv4_cache_t h, int32_t enable)
+{
+    if (!h) return fail(nullptr, KV4_ERR_INVALID_ARGUMENT, "null handle");
+    DeviceGuard g(h->device);
+    h->prof.reset();
+    h->prof.on = enable != 0;
+    return KV4_OK;
+}
+
+kv4_status kv4_profile_read(kv4_cache_t h, kv4_profile* out)
+{
+    if (!h || !out) return fail(h, KV4_ERR_INVALID_ARGUMENT, "null argument");
+    DeviceGuard g(h->device);
+    hipError_t e = h->prof.collect();
+    if (e != hipSuccess) return hip_fail(h, e, "profiling events");
+    *out = h->prof.totals;
     return KV4_OK;
 }
 

@@ -1079,21 +1079,42 @@ hipError_t launch_append(int d, int format, int n_tasks, const AppendArgs& a, hi
 }
 
 template <int D, int G, int F>
-static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream)
+static hipError_t launch_split_t(const DecodeArgs& a, hipStream_t stream)
 {
     const unsigned blocks = (unsigned)((a.n_waves + kWavesPerBlock - 1) / kWavesPerBlock);
     hipLaunchKernelGGL((decode_split_kernel<D, G, F>), dim3(blocks), dim3(64 * kWavesPerBlock), 0, stream, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    return hipGetLastError();
+}
+
+template <int D, int G, int F>
+static hipError_t launch_merge_t(const DecodeArgs& a, hipStream_t stream)
+{
     hipLaunchKernelGGL((merge_kernel<D, G, F != FMT_BF16>), dim3((unsigned)a.n_units), dim3(D), 0, stream, a);
     return hipGetLastError();
 }
 
-hipError_t launch_decode(int d, int g, int format, const DecodeArgs& a, hipStream_t stream)
+hipError_t launch_decode_split(int d, int g, int format, const DecodeArgs& a, hipStream_t stream)
 {
     if (a.n_units <= 0) return hipSuccess;
 #define KV4_DEC_CASE(DD, GG, FF) \
-    if (d == DD && g == GG && format == FF) return launch_decode_t<DD, GG, FF>(a, stream);
+    if (d == DD && g == GG && format == FF) return launch_split_t<DD, GG, FF>(a, stream);
+#define KV4_DEC_G(DD, FF) KV4_DEC_CASE(DD, 1, FF) KV4_DEC_CASE(DD, 2, FF) KV4_DEC_CASE(DD, 4, FF)
+    KV4_DEC_G(64, 0)
+    KV4_DEC_G(64, 1)
+    KV4_DEC_G(64, 2)
+    KV4_DEC_G(128, 0)
+    KV4_DEC_G(128, 1)
+    KV4_DEC_G(128, 2)
+#undef KV4_DEC_G
+#undef KV4_DEC_CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_merge(int d, int g, int format, const DecodeArgs& a, hipStream_t stream)
+{
+    if (a.n_units <= 0) return hipSuccess;
+#define KV4_DEC_CASE(DD, GG, FF) \
+    if (d == DD && g == GG && format == FF) return launch_merge_t<DD, GG, FF>(a, stream);
 #define KV4_DEC_G(DD, FF) KV4_DEC_CASE(DD, 1, FF) KV4_DEC_CASE(DD, 2, FF) KV4_DEC_CASE(DD, 4, FF)
     KV4_DEC_G(64, 0)
     KV4_DEC_G(64, 1)

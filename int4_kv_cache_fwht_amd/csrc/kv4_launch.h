@@ -40,6 +40,7 @@ struct DecodeArgs {
 };
 
 hipError_t launch_append(int d, int format, int n_tasks, const AppendArgs& a, hipStream_t stream);
-hipError_t launch_decode(int d, int g, int format, const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_split(int d, int g, int format, const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_merge(int d, int g, int format, const DecodeArgs& a, hipStream_t stream);
 
 } // namespace kv4
