@@ -72,7 +72,7 @@ def decode_bytes(fmt, lens, w):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for name in ("kv4_kernels.hip", "kv4_launch.h", "kv4_device_types.h"):
+    for name in ("kv4_decode.hip", "kv4_common.cuh", "kv4_launch.h", "kv4_device_types.h"):
         with open(os.path.join(ROOT, "int4_kv_cache_fwht_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

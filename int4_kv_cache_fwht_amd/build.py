@@ -14,6 +14,7 @@ LIB = os.path.join(PKG, "libkv4.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
 ARCH = "gfx950"
+KERNEL_SOURCES = ["kv4_append.hip", "kv4_decode.hip"]
 # -ffp-contract=off: the append's binary32 steps must not fuse into FMAs.
 # -packed-fp32-ops off: no packed fp32 VALU instructions in any kernel.
 HIPFLAGS = [
@@ -44,14 +45,17 @@ def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     hipcc = _hipcc()
     inc = ["-I", INCLUDE, "-I", CSRC]
-    kobj = os.path.join(BUILD_DIR, "kv4_kernels.o")
+    kobjs = []
+    for src in KERNEL_SOURCES:
+        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+        _run([hipcc, "--offload-arch=" + ARCH, *HIPFLAGS, *inc, "-c", os.path.join(CSRC, src), "-o", obj])
+        kobjs.append(obj)
     hobj = os.path.join(BUILD_DIR, "kv4_host.o")
-    _run([hipcc, "--offload-arch=" + ARCH, *HIPFLAGS, *inc, "-c", os.path.join(CSRC, "kv4_kernels.hip"), "-o", kobj])
     rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
     _run([hipcc, "-O2", "-std=c++17", "-fPIC", "-Wall", *inc, "-I", os.path.join(rocm, "include"), "-x", "c++",
           "-D__HIP_PLATFORM_AMD__", "-c", os.path.join(CSRC, "kv4_host.cpp"), "-o", hobj])
     tmp = LIB + ".tmp%d" % os.getpid()
-    _run([hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", kobj, hobj, "-o", tmp])
+    _run([hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", *kobjs, hobj, "-o", tmp])
     os.replace(tmp, LIB)
     if verbose:
         print("built", LIB)

@@ -1,0 +1,306 @@
+// kv4_append.hip -- fused block-FWHT + token-wise quantization + nibble packing + paged store, plus
+// the INT8 copy of protected positions.  Sources: "SAW-INT4: System-Aware 4-Bit KV-Cache
+// Quantization for Real-World LLM Serving", Abstract (a fused rotation-quantization kernel writing
+// into paged KV layouts); "KV4-RL: Unlocking Faster Asynchronous Rollouts for RLVR with INT4 KV
+// Cache Quantization", Abstract (INT8 protection of attention sinks and recent context).
+//
+// Build with -ffp-contract=off: every binary32 step here must stay a single IEEE operation so that
+// codes and scales match the oracle bit for bit.
+#include "kv4_common.cuh"
+
+namespace kv4 {
+
+// ---------------------------------------------------------------------------------------------
+// append
+// ---------------------------------------------------------------------------------------------
+// One wave per (task, kv head).  Lane l handles row l/2 (rows 0..15: K of page slot 0..15,
+// rows 16..31: V of slot 0..15) and half l%2 of its D dims.
+
+template <int N>
+__device__ __forceinline__ void fwht_in_lane(float (&y)[N], int b)
+{
+    // stages h = 1, 2, 4, ... while h < b and h < N, in that order; butterflies (a+c, a-c)
+#pragma unroll
+    for (int h = 1; h < N; h <<= 1) {
+        if (h < b) {
+#pragma unroll
+            for (int i = 0; i < N; i++) {
+                if ((i & h) == 0) {
+                    float a0 = y[i], c0 = y[i + h];
+                    y[i] = a0 + c0;
+                    y[i + h] = a0 - c0;
+                }
+            }
+        }
+    }
+}
+
+// Last stage h = N when b == 2N: partner lane holds the other half of the row.
+template <int N>
+__device__ __forceinline__ void fwht_across_pair(float (&y)[N], int half)
+{
+    const uint32_t sgn = half ? 0x80000000u : 0u;
+#pragma unroll
+    for (int i = 0; i < N; i++) {
+        float own = y[i];
+        float partner = dpp_xor1(own);
+        // half 0: own(dim i) + partner(dim i+N); half 1: partner(dim i) - own(dim i+N)
+        y[i] = partner + as_float(as_uint(own) ^ sgn);
+    }
+}
+
+struct QuantParams {
+    uint32_t s_bits, z_bits;
+    float zf, inv;
+};
+
+// Token-wise scale / zero of one row from its exact min and max; Q = 15 or 255.
+__device__ __forceinline__ QuantParams quant_params(float mn, float mx, float Qf)
+{
+    QuantParams p;
+    p.z_bits = f16_round_down(mn);
+    p.zf = f16_bits_to_float(p.z_bits);
+    float r = mx - p.zf;
+    float t = r / Qf;
+    p.s_bits = f16_round_up(t);
+    float sf = f16_bits_to_float(p.s_bits);
+    p.inv = (sf != 0.0f) ? 1.0f / sf : 0.0f; // s == 0: every code is 0
+    return p;
+}
+
+template <int D, int FMT>
+__global__ __launch_bounds__(64) void append_kernel(AppendArgs a)
+{
+    constexpr int N = D / 2;
+    // V rows staged for the dim-major V layout: INT4 packed rows [16][D/2], INT8 rows [16][D],
+    // bf16 rows [16][D] x 2 B
+    __shared__ __align__(16) uint8_t lds[16 * D * 2];
+    uint8_t* lds_v4 = lds;            // [16][D/2]
+    uint8_t* lds_v8 = lds + 16 * D;   // [16][D]
+
+    const int lane = threadIdx.x;
+    const AppendTask tk = a.tasks[blockIdx.x];
+    const int h = blockIdx.y;
+    const int rho = lane >> 1, half = lane & 1;
+    const bool is_v = rho >= kPageSize;
+    const int slot = rho & (kPageSize - 1);
+    const int s0 = tk.t0 & (kPageSize - 1);
+    const int s1 = s0 + tk.n;
+    const bool active = slot >= s0 && slot < s1;
+    const int t = tk.t0 - s0 + slot;
+    if (lane == 0 && h == 0 && (tk.flags & kTaskNewPage)) a.bt[tk.bt_index] = tk.page;
+    uint8_t* pb = a.pool + ((int64_t)tk.page * a.hkv + h) * a.page_block;
+
+    u32x4 raw[N / 8];
+    if (active) {
+        const uint16_t* src = (is_v ? a.v : a.k) + ((int64_t)(tk.row0 + slot - s0) * a.hkv + h) * D + half * N;
+#pragma unroll
+        for (int q = 0; q < N / 8; q++) raw[q] = *(const u32x4*)(src + 8 * q);
+    } else {
+#pragma unroll
+        for (int q = 0; q < N / 8; q++) raw[q] = (u32x4){0u, 0u, 0u, 0u};
+    }
+
+    if constexpr (FMT == FMT_BF16) {
+        uint16_t* lds_bf = (uint16_t*)lds; // [16][D]
+        if (active) {
+            if (!is_v) {
+#pragma unroll
+                for (int q = 0; q < N / 8; q++) *(u32x4*)(pb + (half * (N / 8) + q) * 256 + slot * 16) = raw[q];
+            } else {
+#pragma unroll
+                for (int q = 0; q < N / 8; q++) *(u32x4*)(lds_bf + slot * D + half * N + 8 * q) = raw[q];
+            }
+        }
+        __syncthreads();
+        // dim-major V: [D][16 slots x bf16]
+#pragma unroll
+        for (int dd = 0; dd < D / 64; dd++) {
+            const int d = dd * 64 + lane;
+            uint32_t* dst = (uint32_t*)(pb + 32 * D + d * 32);
+            uint32_t w[8];
+#pragma unroll
+            for (int j = 0; j < 8; j++) w[j] = (tk.n < 16) ? dst[j] : 0u;
+            for (int s = s0; s < s1; s++) {
+                uint32_t v = lds_bf[s * D + d];
+                int sh = (s & 1) * 16;
+#pragma unroll
+                for (int j = 0; j < 8; j++)
+                    if (j == (s >> 1)) w[j] = (w[j] & ~(0xFFFFu << sh)) | (v << sh);
+            }
+#pragma unroll
+            for (int j = 0; j < 8; j += 4) *(u32x4*)(dst + j) = (u32x4){w[j], w[j + 1], w[j + 2], w[j + 3]};
+        }
+        return;
+    } else {
+        // ---- rotate ----
+        float y[N];
+#pragma unroll
+        for (int q = 0; q < N / 8; q++) {
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                y[8 * q + 2 * j] = as_float(raw[q][j] << 16);
+                y[8 * q + 2 * j + 1] = as_float(raw[q][j] & 0xFFFF0000u);
+            }
+        }
+        fwht_in_lane<N>(y, a.block);
+        if (a.block == D) fwht_across_pair<N>(y, half);
+        if (a.block > 1) {
+#pragma unroll
+            for (int i = 0; i < N; i++) y[i] = y[i] * a.cb;
+        }
+        // ---- row min / max ----
+        float mn = y[0], mx = y[0];
+#pragma unroll
+        for (int i = 1; i < N; i++) {
+            mn = fminf(mn, y[i]);
+            mx = fmaxf(mx, y[i]);
+        }
+        mn = fminf(mn, dpp_xor1(mn));
+        mx = fmaxf(mx, dpp_xor1(mx));
+
+        const bool prot = (FMT == FMT_INT4_PROT) && active && is_protected(t, tk.len_new, a.sinks, a.recent);
+
+        if constexpr (FMT == FMT_INT4_PROT) {
+            // ---- INT4 codes, natural nibble order: byte k = code[2k] | code[2k+1] << 4 ----
+            const QuantParams qp = quant_params(mn, mx, 15.0f);
+            uint32_t pk[N / 8];
+#pragma unroll
+            for (int q = 0; q < N / 8; q++) {
+                uint32_t e = 0, o = 0;
+                float u0 = (y[8 * q + 0] - qp.zf) * qp.inv, u1 = (y[8 * q + 1] - qp.zf) * qp.inv;
+                float u2 = (y[8 * q + 2] - qp.zf) * qp.inv, u3 = (y[8 * q + 3] - qp.zf) * qp.inv;
+                float u4 = (y[8 * q + 4] - qp.zf) * qp.inv, u5 = (y[8 * q + 5] - qp.zf) * qp.inv;
+                float u6 = (y[8 * q + 6] - qp.zf) * qp.inv, u7 = (y[8 * q + 7] - qp.zf) * qp.inv;
+                e = __builtin_amdgcn_cvt_pk_u8_f32(u0, 0, e);
+                e = __builtin_amdgcn_cvt_pk_u8_f32(u2, 1, e);
+                e = __builtin_amdgcn_cvt_pk_u8_f32(u4, 2, e);
+                e = __builtin_amdgcn_cvt_pk_u8_f32(u6, 3, e);
+                o = __builtin_amdgcn_cvt_pk_u8_f32(u1, 0, o);
+                o = __builtin_amdgcn_cvt_pk_u8_f32(u3, 1, o);
+                o = __builtin_amdgcn_cvt_pk_u8_f32(u5, 2, o);
+                o = __builtin_amdgcn_cvt_pk_u8_f32(u7, 3, o);
+                pk[q] = e | (o << 4);
+            }
+            if (active) {
+                if (!is_v) {
+                    // K: [D/32 chunks][16 slots][16 B]; this half covers chunks half*N/32 ..
+#pragma unroll
+                    for (int c = 0; c < N / 32; c++)
+                        *(u32x4*)(pb + (half * (N / 32) + c) * 256 + slot * 16) =
+                            (u32x4){pk[4 * c], pk[4 * c + 1], pk[4 * c + 2], pk[4 * c + 3]};
+                } else {
+#pragma unroll
+                    for (int c = 0; c < N / 32; c++)
+                        *(u32x4*)(lds_v4 + slot * (D / 2) + half * (N / 2) + 16 * c) =
+                            (u32x4){pk[4 * c], pk[4 * c + 1], pk[4 * c + 2], pk[4 * c + 3]};
+                }
+                if (half == 0)
+                    *(uint32_t*)(pb + 16 * D + slot * 8 + (is_v ? 4 : 0)) = qp.s_bits | (qp.z_bits << 16);
+            }
+        }
+
+        // ---- INT8 codes: protected positions (INT4_PROT) or every position (INT8 format) ----
+        const bool want8 = (FMT == FMT_INT8) ? active : prot;
+        if (__ballot(want8) != 0ull) {
+            const QuantParams qp = quant_params(mn, mx, 255.0f);
+            uint32_t cb8[N / 4];
+#pragma unroll
+            for (int q = 0; q < N / 4; q++) {
+                uint32_t w = 0;
+                w = __builtin_amdgcn_cvt_pk_u8_f32((y[4 * q + 0] - qp.zf) * qp.inv, 0, w);
+                w = __builtin_amdgcn_cvt_pk_u8_f32((y[4 * q + 1] - qp.zf) * qp.inv, 1, w);
+                w = __builtin_amdgcn_cvt_pk_u8_f32((y[4 * q + 2] - qp.zf) * qp.inv, 2, w);
+                w = __builtin_amdgcn_cvt_pk_u8_f32((y[4 * q + 3] - qp.zf) * qp.inv, 3, w);
+                cb8[q] = w;
+            }
+            if (want8) {
+                uint8_t* tb;
+                int s8;
+                if (FMT == FMT_INT8) {
+                    tb = pb;
+                    s8 = slot;
+                } else {
+                    const int u = (t < a.sinks) ? t : a.sinks + t % a.recent;
+                    tb = a.int8_pool + (((int64_t)tk.seq * a.hkv + h) * a.int8_tiles + (u >> 4)) * a.int8_tile;
+                    s8 = u & 15;
+                }
+                if (!is_v) {
+                    // K8: [D/16 chunks][16 slots][16 B]; this half covers chunks half*N/16 ..
+#pragma unroll
+                    for (int c = 0; c < N / 16; c++)
+                        *(u32x4*)(tb + (half * (N / 16) + c) * 256 + s8 * 16) =
+                            (u32x4){cb8[4 * c], cb8[4 * c + 1], cb8[4 * c + 2], cb8[4 * c + 3]};
+                } else {
+#pragma unroll
+                    for (int c = 0; c < N / 16; c++)
+                        *(u32x4*)(lds_v8 + slot * D + half * N + 16 * c) =
+                            (u32x4){cb8[4 * c], cb8[4 * c + 1], cb8[4 * c + 2], cb8[4 * c + 3]};
+                }
+                if (half == 0) *(uint32_t*)(tb + 32 * D + s8 * 8 + (is_v ? 4 : 0)) = qp.s_bits | (qp.z_bits << 16);
+            }
+        }
+        __syncthreads();
+
+        // ---- dim-major V stores: lane = dim ----
+#pragma unroll
+        for (int dd = 0; dd < D / 64; dd++) {
+            const int d = dd * 64 + lane;
+            if constexpr (FMT == FMT_INT4_PROT) {
+                // [D][8 B]: nibble s = slot s
+                u32x2* dst = (u32x2*)(pb + 8 * D + d * 8);
+                u32x2 w = (tk.n < 16) ? *dst : (u32x2){0u, 0u};
+                for (int s = s0; s < s1; s++) {
+                    uint32_t nib = (lds_v4[s * (D / 2) + (d >> 1)] >> ((d & 1) * 4)) & 0xFu;
+                    int sh = (s & 7) * 4;
+                    if (s < 8)
+                        w.x = (w.x & ~(0xFu << sh)) | (nib << sh);
+                    else
+                        w.y = (w.y & ~(0xFu << sh)) | (nib << sh);
+                }
+                *dst = w;
+                // INT8 copies of protected positions: one byte per (position, dim)
+                for (int s = s0; s < s1; s++) {
+                    const int ts = tk.t0 - s0 + s;
+                    if (!is_protected(ts, tk.len_new, a.sinks, a.recent)) continue;
+                    const int u = (ts < a.sinks) ? ts : a.sinks + ts % a.recent;
+                    uint8_t* tb = a.int8_pool + (((int64_t)tk.seq * a.hkv + h) * a.int8_tiles + (u >> 4)) * a.int8_tile;
+                    tb[16 * D + d * 16 + (u & 15)] = lds_v8[s * D + d];
+                }
+            } else {
+                // INT8 format: [D][16 B], byte s = slot s
+                u32x4* dst = (u32x4*)(pb + 16 * D + d * 16);
+                u32x4 w = (tk.n < 16) ? *dst : (u32x4){0u, 0u, 0u, 0u};
+                for (int s = s0; s < s1; s++) {
+                    uint32_t v = lds_v8[s * D + d];
+                    int sh = (s & 3) * 8;
+#pragma unroll
+                    for (int j = 0; j < 4; j++)
+                        if (j == (s >> 2)) w[j] = (w[j] & ~(0xFFu << sh)) | (v << sh);
+                }
+                *dst = w;
+            }
+        }
+    }
+}
+
+hipError_t launch_append(int d, int format, int n_tasks, const AppendArgs& a, hipStream_t stream)
+{
+    if (n_tasks <= 0) return hipSuccess;
+    dim3 grid((unsigned)n_tasks, (unsigned)a.hkv), block(64);
+#define KV4_APPEND_CASE(DD, FF)                                                          \
+    if (d == DD && format == FF) {                                                       \
+        hipLaunchKernelGGL((append_kernel<DD, FF>), grid, block, 0, stream, a);          \
+        return hipGetLastError();                                                        \
+    }
+    KV4_APPEND_CASE(64, 0)
+    KV4_APPEND_CASE(64, 1)
+    KV4_APPEND_CASE(64, 2)
+    KV4_APPEND_CASE(128, 0)
+    KV4_APPEND_CASE(128, 1)
+    KV4_APPEND_CASE(128, 2)
+#undef KV4_APPEND_CASE
+    return hipErrorInvalidValue;
+}
+
+} // namespace kv4
