@@ -74,10 +74,12 @@ typedef struct kv4_config {
  *                  dims 32c..32c+31 of token t, byte k = code[2k] | code[2k+1] << 4
  *   [8D, 16D)      V codes  [D dims][8 B]; byte k of dim d = code(slot 2k) | code(slot 2k+1) << 4
  *   [16D, 16D+128) scales   [16 slots][4 x fp16] = (K scale, K zero, V scale, V zero)
- * INT8 tile (INT8_PROT slots and INT8-format pages), int8_tile_bytes = 32*D + 128:
- *   [0, 16D)       K codes  [D/16 chunks][16 slots][16 B] (chunk c = dims 16c..16c+15, one byte each)
- *   [16D, 32D)     V codes  [D dims][16 B]; byte k = code of slot k
- *   [32D, 32D+128) scales   [16 slots][4 x fp16] as above
+ * INT8 tile (INT4_PROT protection slots and INT8-format pages), int8_tile_bytes = 32*D + 256:
+ *   two blocks x = 0, 1 of 16*D + 128 bytes each, shaped like an INT4 page block; block x holds
+ *   [0, 8D)        K codes  [D/32 chunks][16 slots][16 B]; piece c of slot t = dims
+ *                  x*D/2 + 16c .. x*D/2 + 16c + 15 of token t, one byte each
+ *   [8D, 16D)      V codes  [D dims][8 B]; byte j of dim d = code of slot 8x + j
+ *   [16D, 16D+128) scales   [16 slots][4 x fp16] as above (the same in both blocks)
  * BF16 page block, page_block_bytes = 64*D:
  *   [0, 32D)       K        [D/8 chunks][16 slots][8 x bf16]
  *   [32D, 64D)     V        [D dims][16 slots x bf16]

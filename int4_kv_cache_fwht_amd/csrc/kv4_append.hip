@@ -225,11 +225,13 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a)
                     tb = a.int8_pool + (((int64_t)tk.seq * a.hkv + h) * a.int8_tiles + (u >> 4)) * a.int8_tile;
                     s8 = u & 15;
                 }
+                // the tile is two blocks of 16D + 128 bytes; block `half` holds K dims half*D/2 ..
+                uint8_t* bh = tb + half * (16 * D + 128);
                 if (!is_v) {
-                    // K8: [D/16 chunks][16 slots][16 B]; this half covers chunks half*N/16 ..
+                    // K8 of this half: [D/32 chunks][16 slots][16 B]
 #pragma unroll
                     for (int c = 0; c < N / 16; c++)
-                        *(u32x4*)(tb + (half * (N / 16) + c) * 256 + s8 * 16) =
+                        *(u32x4*)(bh + c * 256 + s8 * 16) =
                             (u32x4){cb8[4 * c], cb8[4 * c + 1], cb8[4 * c + 2], cb8[4 * c + 3]};
                 } else {
 #pragma unroll
@@ -237,7 +239,8 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a)
                         *(u32x4*)(lds_v8 + slot * D + half * N + 16 * c) =
                             (u32x4){cb8[4 * c], cb8[4 * c + 1], cb8[4 * c + 2], cb8[4 * c + 3]};
                 }
-                if (half == 0) *(uint32_t*)(tb + 32 * D + s8 * 8 + (is_v ? 4 : 0)) = qp.s_bits | (qp.z_bits << 16);
+                // scales: a copy in each block
+                *(uint32_t*)(bh + 16 * D + s8 * 8 + (is_v ? 4 : 0)) = qp.s_bits | (qp.z_bits << 16);
             }
         }
         __syncthreads();
@@ -265,12 +268,14 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a)
                     if (!is_protected(ts, tk.len_new, a.sinks, a.recent)) continue;
                     const int u = (ts < a.sinks) ? ts : a.sinks + ts % a.recent;
                     uint8_t* tb = a.int8_pool + (((int64_t)tk.seq * a.hkv + h) * a.int8_tiles + (u >> 4)) * a.int8_tile;
-                    tb[16 * D + d * 16 + (u & 15)] = lds_v8[s * D + d];
+                    // V of slot u % 16: block (u % 16) / 8, [D][8 B], byte (u % 8)
+                    tb[((u >> 3) & 1) * (16 * D + 128) + 8 * D + d * 8 + (u & 7)] = lds_v8[s * D + d];
                 }
             } else {
-                // INT8 format: [D][16 B], byte s = slot s
-                u32x4* dst = (u32x4*)(pb + 16 * D + d * 16);
-                u32x4 w = (tk.n < 16) ? *dst : (u32x4){0u, 0u, 0u, 0u};
+                // INT8 format: block x = slot / 8 holds V as [D][8 B], byte j = slot 8x + j
+                u32x2* dst0 = (u32x2*)(pb + 8 * D + d * 8);
+                u32x2* dst1 = (u32x2*)(pb + (16 * D + 128) + 8 * D + d * 8);
+                u32x4 w = (tk.n < 16) ? (u32x4){(*dst0).x, (*dst0).y, (*dst1).x, (*dst1).y} : (u32x4){0u, 0u, 0u, 0u};
                 for (int s = s0; s < s1; s++) {
                     uint32_t v = lds_v8[s * D + d];
                     int sh = (s & 3) * 8;
@@ -278,7 +283,8 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a)
                     for (int j = 0; j < 4; j++)
                         if (j == (s >> 2)) w[j] = (w[j] & ~(0xFFu << sh)) | (v << sh);
                 }
-                *dst = w;
+                *dst0 = (u32x2){w[0], w[1]};
+                *dst1 = (u32x2){w[2], w[3]};
             }
         }
     }

@@ -129,6 +129,13 @@ __device__ __forceinline__ float4_t mfma_h(half4_t a, half4_t b, float4_t c)
     return __builtin_amdgcn_mfma_f32_4x4x4f16(a, b, c, 4, ABID, 0);
 }
 
+// A of block ABID of each half wave (blocks 0..7, 8..15) is broadcast to the blocks of that half
+template <int ABID>
+__device__ __forceinline__ float4_t mfma_h_half(half4_t a, half4_t b, float4_t c)
+{
+    return __builtin_amdgcn_mfma_f32_4x4x4f16(a, b, c, 3, ABID, 0);
+}
+
 template <int ABID>
 __device__ __forceinline__ float4_t mfma_bf(short4_t a, short4_t b, float4_t c)
 {

@@ -13,22 +13,26 @@
 //          rotated, power-of-two-normalised query split into hi + lo fp16 is the A operand,
 //          broadcast from one lane quad to all 16 blocks (CBSZ = 4, ABID = quad).  A score is
 //          s * (q . code) + z * sum(q): keys are never dequantised element by element.
-//   INT8:  32 protection slots (or 2 INT8 pages), lanes 0..31, same scheme with byte codes.
+//   INT8:  32 slots (2 tiles), lane = slot within each half wave; the two half waves take the two
+//          halves of the head dimension, the A operand is broadcast per half (CBSZ = 3) and the
+//          two partial scores are added across halves.
 //   BF16:  1 page = 16 positions, lanes 0..15, raw bf16 operands.
 // PV runs on the same MFMA with lane = output dim: V codes (dim-major in the page) are the B
 // operand and p*s (split hi + lo fp16 after an fp32 exchange through LDS) is broadcast; the
 // zero-point term sum_t p_t z_t is accumulated per lane and added once per unit.
 //
-// Latency hiding: the next step's loads are issued before the current step's arithmetic
-// (ping-pong buffers).  Every load of a step is issued unconditionally -- indices past the end are
-// clamped onto the last valid page, whose lines the same step already reads, and the duplicated
-// positions are masked -- so that the waitcnt counters never have to drain the prefetch.  Page ids
-// and the plan are read with scalar loads (a separate counter) one step ahead.
+// Latency hiding (quantized formats): a unit's INT8 and INT4 steps run as one pipeline.  An INT8
+// tile is stored as two blocks shaped like an INT4 page block, so both step types issue the same
+// 13 vector loads (4 x 16 B of K, 8 B of scales, 8 x 8 B of V) into the same registers and only
+// the four block addresses differ: the next step's loads are always in flight during the current
+// step's arithmetic and the wait counters never drain them.  Loads past the end repeat the last
+// step's addresses (cached lines) and are never used.  Page ids are read with scalar loads (their
+// own counter) two steps ahead.
 #include "kv4_common.cuh"
 
 namespace kv4 {
 
-constexpr int kLdsQBytes = 4 * 128 * 4; // rotated query, G x D fp32
+constexpr int kLdsQBytes = 4 * 128 * 4; // rotated query, G x D fp32 (raw bf16 query first)
 constexpr int kLdsPBytes = 64 * 16;     // per-step probability exchange (fp32)
 constexpr int kLdsPerWave = kLdsQBytes + kLdsPBytes;
 // Running max: a full reduction (and rescale) happens only when some score exceeds the current
@@ -60,60 +64,60 @@ __device__ __forceinline__ DecodeUnit ld_unit(const DecodeUnit* units, int u)
 // s_waitcnt vmcnt(0), other counters untouched (gfx9 encoding)
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Identity DPP move: keeps a wave-uniform value in a vector register (frees scalar registers).
+__device__ __forceinline__ float in_vgpr(float x)
+{
+    return as_float((uint32_t)__builtin_amdgcn_update_dpp(0, (int)as_uint(x), 0xE4, 0xF, 0xF, false));
+}
+
+// Block indices of one step (page ids or INT8 tile indices), wave-uniform.
+struct Ids {
+    int32_t i0, i1, i2, i3;
+};
+
 template <int D, int G, int FMT>
 struct DecodeWave {
     static constexpr int NHV = D / 64;   // output dims per lane
     static constexpr int NPAIR = D / 32; // A-operand VGPR pairs of the INT4 / INT8 query sets
     static constexpr int NPAIR_BF = D / 64;
-    static constexpr int NQ = (FMT == FMT_BF16) ? 2 * NPAIR_BF : G * NHV; // raw query registers
+    static constexpr int NK = D / 32;    // 16-byte K pieces per lane and step
+    static constexpr int NV = 4 * NHV;   // 8-byte V pieces per lane and step
+    static constexpr int QLANES = G * D / 8;
 
-    struct Int4Data {
-        u32x4 kc[D / 32];
+    // One step's data for the quantized formats.
+    //   INT4: k[c] = 16 B piece c of the lane's slot (dims 32c..32c+31), sz = its scales,
+    //         v[q * NHV + hv] = 8 B of dim 64 hv + lane in page q.
+    //   INT8: k[c] = dims D/2 * half + 16c .. +15 of the lane's slot (half = lane / 32, slot =
+    //         lane % 32), sz = its scales, v[q * NHV + hv] = slots 16 (q % 2) + 8 (q / 2) .. +7 of
+    //         dim 64 hv + lane.
+    struct Buf {
+        u32x4 k[NK];
         u32x2 sz;
-        u32x2 vc[kInt4StepPages][NHV];
-    };
-    struct Int8Data {
-        u32x4 k8[D / 16];
-        u32x2 sz;
-        u32x4 v8[2][NHV];
+        u32x2 v[NV];
     };
 
     const DecodeArgs& a;
     const int lane;
     uint8_t* lds_q;
     uint8_t* lds_p;
+    const int64_t w;     // wave index (partial slot of unit u is w + u)
+    const int64_t s_end; // one past the wave's last global step
+    const int n8;        // INT8 steps at the start of an INT4_PROT unit
 
     half4_t A4[NPAIR], A8[NPAIR];
     short4_t Abf[NPAIR_BF];
     float4_t acc[NHV][2]; // two accumulation chains per output half
     float m[4], lsum[4], zsum[4], F[4], sumq[4];
 
-    __device__ DecodeWave(const DecodeArgs& args, int ln, uint8_t* lq, uint8_t* lp)
-        : a(args), lane(ln), lds_q(lq), lds_p(lp) {}
-
-    // ---- query: raw loads (issued first), then rotate / normalise / split into A operands ----
-    __device__ __forceinline__ void load_q(const DecodeUnit& U, uint32_t (&qr)[NQ])
+    __device__ DecodeWave(const DecodeArgs& args, int ln, uint8_t* lq, uint8_t* lp, int64_t wi, int64_t se)
+        : a(args), lane(ln), lds_q(lq), lds_p(lp), w(wi), s_end(se),
+          n8((FMT == FMT_INT4_PROT && args.sinks + args.recent > 0)
+                 ? (args.sinks + args.recent + kInt8StepSlots - 1) / kInt8StepSlots
+                 : 0)
     {
-        const uint16_t* qrow = a.q + ((int64_t)U.entry * (a.hkv * G) + U.head * G) * D;
-        if constexpr (FMT == FMT_BF16) {
-            // A step m = dims 4m..4m+3 of head lane&3, pair m/16, quad m%16
-            const int s = lane >> 2, i = lane & 3;
-            const int ic = i < G ? i : 0;
-#pragma unroll
-            for (int v = 0; v < NPAIR_BF; v++) {
-                const uint32_t* src = (const uint32_t*)(qrow + ic * D + 4 * (16 * v + s));
-                qr[2 * v] = src[0];
-                qr[2 * v + 1] = src[1];
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < G; i++)
-#pragma unroll
-                for (int j = 0; j < NHV; j++) qr[i * NHV + j] = qrow[i * D + 64 * j + lane];
-        }
     }
 
-    __device__ void prologue(const uint32_t (&qr)[NQ], bool need4, bool need8)
+    __device__ __forceinline__ void reset_state()
     {
 #pragma unroll
         for (int i = 0; i < 4; i++) {
@@ -123,118 +127,120 @@ struct DecodeWave {
         }
 #pragma unroll
         for (int hv = 0; hv < NHV; hv++) acc[hv][0] = acc[hv][1] = (float4_t){0.f, 0.f, 0.f, 0.f};
+    }
 
-        if constexpr (FMT == FMT_BF16) {
-            const bool live = (lane & 3) < G;
+    // ---- query prologue of a unit (quantized formats): rotate, normalise, split into A operands ----
+    __device__ void prologue_q(const u32x4& qraw)
+    {
+        reset_state();
+        // raw bf16 rows through LDS into the layout "lane holds dims lane + 64 j of each head"
+        uint16_t* raw = (uint16_t*)lds_q;
+        if (lane < QLANES) *(u32x4*)(raw + 8 * lane) = qraw;
+        wave_lds_sync();
+        float qv[G][NHV];
 #pragma unroll
-            for (int v = 0; v < NPAIR_BF; v++) Abf[v] = to_short4(live ? qr[2 * v] : 0u, live ? qr[2 * v + 1] : 0u);
+        for (int i = 0; i < G; i++)
 #pragma unroll
-            for (int i2 = 0; i2 < 4; i2++) {
-                F[i2] = a.scale_log2;
-                sumq[i2] = 0.f;
-            }
-        } else {
-            // lane holds dims lane + 64*j of each head; block FWHT in fp32 (any stage order)
-            float qv[G][NHV];
+            for (int j = 0; j < NHV; j++) qv[i][j] = as_float((uint32_t)raw[i * D + 64 * j + lane] << 16);
+        wave_lds_sync();
+        // block FWHT in fp32 (any stage order)
+        for (int hh = 1; hh < a.block && hh < 64; hh <<= 1) {
 #pragma unroll
             for (int i = 0; i < G; i++)
 #pragma unroll
-                for (int j = 0; j < NHV; j++) qv[i][j] = as_float(qr[i * NHV + j] << 16);
-            for (int hh = 1; hh < a.block && hh < 64; hh <<= 1) {
-#pragma unroll
-                for (int i = 0; i < G; i++)
-#pragma unroll
-                    for (int j = 0; j < NHV; j++) {
-                        const float other = __shfl_xor(qv[i][j], hh, 64);
-                        qv[i][j] = (lane & hh) ? other - qv[i][j] : qv[i][j] + other;
-                    }
-            }
-            if constexpr (NHV > 1) {
-                if (a.block > 64) {
-#pragma unroll
-                    for (int i = 0; i < G; i++) {
-                        const float a0 = qv[i][0], a1 = qv[i][1];
-                        qv[i][0] = a0 + a1;
-                        qv[i][1] = a0 - a1;
-                    }
+                for (int j = 0; j < NHV; j++) {
+                    const float other = __shfl_xor(qv[i][j], hh, 64);
+                    qv[i][j] = (lane & hh) ? other - qv[i][j] : qv[i][j] + other;
                 }
-            }
-            float* lq = (float*)lds_q;
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                if (i < G) {
-                    float mx = 0.f;
-#pragma unroll
-                    for (int j = 0; j < NHV; j++) {
-                        qv[i][j] = qv[i][j] * a.cb;
-                        mx = fmaxf(mx, fabsf(qv[i][j]));
-                    }
-                    mx = wave_max_u(mx);
-                    int e = 0;
-                    if (mx > 0.f) frexpf(mx, &e);
-                    const int eq = (mx > 0.f) ? 15 - e : 0; // max |q| * 2^eq in [2^14, 2^15)
-                    float sq = 0.f;
-#pragma unroll
-                    for (int j = 0; j < NHV; j++) {
-                        qv[i][j] = ldexpf(qv[i][j], eq);
-                        sq += qv[i][j];
-                        lq[i * D + 64 * j + lane] = qv[i][j];
-                    }
-                    sumq[i] = wave_sum_u(sq);
-                    F[i] = a.scale_log2 * ldexpf(1.0f, -eq);
-                } else {
-                    sumq[i] = 0.f;
-                    F[i] = 0.f;
-                }
-            }
-            wave_lds_sync();
-            const int s = lane >> 2, i = lane & 3;
-            if (need4) {
-                // INT4 step m = 16c + 4wd + 2gp + hl: pair c, quad m % 16; the dims of word
-                // u = 4c + wd are fed in the order (8u, 8u+4, 8u+1, 8u+5) (gp 0) or
-                // (8u+2, 8u+6, 8u+3, 8u+7) (gp 1); the odd dims arrive multiplied by 16.
-                const int hl = s & 1, gp = (s >> 1) & 1, wd = s >> 2;
-#pragma unroll
-                for (int c = 0; c < NPAIR; c++) {
-                    const int d0 = 8 * (4 * c + wd) + 2 * gp;
-                    float x[4] = {0.f, 0.f, 0.f, 0.f};
-                    if (i < G) {
-                        x[0] = lq[i * D + d0];
-                        x[1] = lq[i * D + d0 + 4];
-                        x[2] = lq[i * D + d0 + 1] * 0.0625f;
-                        x[3] = lq[i * D + d0 + 5] * 0.0625f;
-                    }
-                    _Float16 r[4];
-#pragma unroll
-                    for (int k = 0; k < 4; k++) {
-                        const _Float16 hi16 = (_Float16)x[k];
-                        r[k] = hl ? (_Float16)(x[k] - (float)hi16) : hi16;
-                    }
-                    A4[c] = (half4_t){r[0], r[1], r[2], r[3]};
-                }
-            }
-            if (need8) {
-                // INT8 step m = 2u + hl (dims 4u..4u+3): pair m / 16, quad m % 16
-                const int hl = s & 1;
-#pragma unroll
-                for (int v = 0; v < NPAIR; v++) {
-                    const int u = 8 * v + (s >> 1);
-                    float x[4] = {0.f, 0.f, 0.f, 0.f};
-                    if (i < G) {
-#pragma unroll
-                        for (int k = 0; k < 4; k++) x[k] = lq[i * D + 4 * u + k];
-                    }
-                    _Float16 r[4];
-#pragma unroll
-                    for (int k = 0; k < 4; k++) {
-                        const _Float16 hi16 = (_Float16)x[k];
-                        r[k] = hl ? (_Float16)(x[k] - (float)hi16) : hi16;
-                    }
-                    A8[v] = (half4_t){r[0], r[1], r[2], r[3]};
-                }
-            }
-            wave_lds_sync();
         }
+        if constexpr (NHV > 1) {
+            if (a.block > 64) {
+#pragma unroll
+                for (int i = 0; i < G; i++) {
+                    const float a0 = qv[i][0], a1 = qv[i][1];
+                    qv[i][0] = a0 + a1;
+                    qv[i][1] = a0 - a1;
+                }
+            }
+        }
+        float* lq = (float*)lds_q;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            if (i < G) {
+                float mx = 0.f;
+#pragma unroll
+                for (int j = 0; j < NHV; j++) {
+                    qv[i][j] = qv[i][j] * a.cb;
+                    mx = fmaxf(mx, fabsf(qv[i][j]));
+                }
+                mx = wave_max_u(mx);
+                int e = 0;
+                if (mx > 0.f) frexpf(mx, &e);
+                const int eq = (mx > 0.f) ? 15 - e : 0; // max |q| * 2^eq in [2^14, 2^15)
+                float sq = 0.f;
+#pragma unroll
+                for (int j = 0; j < NHV; j++) {
+                    qv[i][j] = ldexpf(qv[i][j], eq);
+                    sq += qv[i][j];
+                    lq[i * D + 64 * j + lane] = qv[i][j];
+                }
+                sumq[i] = in_vgpr(wave_sum_u(sq));
+                F[i] = in_vgpr(a.scale_log2 * ldexpf(1.0f, -eq));
+            } else {
+                sumq[i] = 0.f;
+                F[i] = 0.f;
+            }
+        }
+        wave_lds_sync();
+        const int i = lane & 3;
+        if (FMT == FMT_INT4_PROT) {
+            // INT4 step m = 16c + 4wd + 2gp + hl: pair c, quad m % 16 (all 16 blocks); the dims of
+            // word u = 4c + wd are fed in the order (8u, 8u+4, 8u+1, 8u+5) (gp 0) or
+            // (8u+2, 8u+6, 8u+3, 8u+7) (gp 1); the odd dims arrive multiplied by 16.
+            const int s = lane >> 2;
+            const int hl = s & 1, gp = (s >> 1) & 1, wd = s >> 2;
+#pragma unroll
+            for (int c = 0; c < NPAIR; c++) {
+                const int d0 = 8 * (4 * c + wd) + 2 * gp;
+                float x[4] = {0.f, 0.f, 0.f, 0.f};
+                if (i < G) {
+                    x[0] = lq[i * D + d0];
+                    x[1] = lq[i * D + d0 + 4];
+                    x[2] = lq[i * D + d0 + 1] * 0.0625f;
+                    x[3] = lq[i * D + d0 + 5] * 0.0625f;
+                }
+                _Float16 r[4];
+#pragma unroll
+                for (int k = 0; k < 4; k++) {
+                    const _Float16 hi16 = (_Float16)x[k];
+                    r[k] = hl ? (_Float16)(x[k] - (float)hi16) : hi16;
+                }
+                A4[c] = (half4_t){r[0], r[1], r[2], r[3]};
+            }
+        }
+        if (FMT == FMT_INT8 || n8 > 0) {
+            // INT8 step m = 8v + s of half h (lane = 32h + 4s + i): pair v, block s of the half;
+            // word u = m / 2 holds dims h*D/2 + 4u .. +3, hl = m % 2
+            const int h = lane >> 5, s = (lane >> 2) & 7;
+#pragma unroll
+            for (int v = 0; v < NPAIR; v++) {
+                const int mm = 8 * v + s, u = mm >> 1, hl = mm & 1;
+                const int d0 = h * (D / 2) + 4 * u;
+                float x[4] = {0.f, 0.f, 0.f, 0.f};
+                if (i < G) {
+#pragma unroll
+                    for (int k = 0; k < 4; k++) x[k] = lq[i * D + d0 + k];
+                }
+                _Float16 r[4];
+#pragma unroll
+                for (int k = 0; k < 4; k++) {
+                    const _Float16 hi16 = (_Float16)x[k];
+                    r[k] = hl ? (_Float16)(x[k] - (float)hi16) : hi16;
+                }
+                A8[v] = (half4_t){r[0], r[1], r[2], r[3]};
+            }
+        }
+        wave_lds_sync();
     }
 
     // ---- online softmax over one step: sc[i] are log2-domain scores (-inf where masked) ----
@@ -264,7 +270,7 @@ struct DecodeWave {
                     }
                     lsum[i] *= alpha;
                     zsum[i] *= alpha;
-                    m[i] = mnew[i];
+                    m[i] = in_vgpr(mnew[i]);
                 }
             }
         }
@@ -312,39 +318,95 @@ struct DecodeWave {
         Alo = to_half4(__builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23));
     }
 
-    // ================================ INT4 steps ================================
-    // page ids of the step whose first page is p_first (clamped to the last INT4 page)
-    __device__ __forceinline__ void int4_ids(const DecodeUnit& U, int p_first, int p_end, int32_t (&id)[4])
+    // ================================ steps of one unit ================================
+    __device__ __forceinline__ bool is_int8_step(int k) const { return FMT == FMT_INT8 || k < n8; }
+
+    // INT4 pages [p0, p1) of the positions [S, L - R) read from INT4 (empty when L <= S + R)
+    __device__ __forceinline__ int int4_p1(int len) const
+    {
+        const int hi4 = len - a.recent;
+        return hi4 > a.sinks ? (hi4 - 1) / kPageSize + 1 : 0;
+    }
+
+    // Block indices of step k: INT4 = 4 page ids (clamped to the last INT4 page); INT8 format =
+    // the 2 pages' ids and INT8 protection = the 2 tile indices, each listed twice (tile j % 2,
+    // block j / 2 of the tile).
+    __device__ __forceinline__ Ids step_ids(const DecodeUnit& U, int k, int p1) const
     {
         const int32_t* btr = a.bt + (int64_t)U.seq * a.max_pps;
-        const int last = p_end - 1;
-#pragma unroll
-        for (int q = 0; q < kInt4StepPages; q++) id[q] = ld_uniform(btr + min(p_first + q, last));
-    }
-
-    __device__ __forceinline__ void int4_load(const DecodeUnit& U, const int32_t (&id)[4], Int4Data& dd)
-    {
-        const int pj = lane >> 4, t16 = lane & 15;
-        const int64_t stride = (int64_t)a.hkv * a.page_block;
-        const int64_t hoff = (int64_t)U.head * a.page_block;
-        const int32_t my_id = pj == 0 ? id[0] : pj == 1 ? id[1] : pj == 2 ? id[2] : id[3];
-        const uint8_t* pbl = a.pool + (int64_t)my_id * stride + hoff;
-#pragma unroll
-        for (int c = 0; c < D / 32; c++) dd.kc[c] = *(const u32x4*)(pbl + c * 256 + t16 * 16);
-        dd.sz = *(const u32x2*)(pbl + 16 * D + t16 * 8);
-#pragma unroll
-        for (int q = 0; q < kInt4StepPages; q++) {
-            const uint8_t* pbq = a.pool + (int64_t)id[q] * stride + hoff;
-#pragma unroll
-            for (int hv = 0; hv < NHV; hv++) dd.vc[q][hv] = *(const u32x2*)(pbq + 8 * D + (64 * hv + lane) * 8);
+        Ids id;
+        if (FMT == FMT_INT8) {
+            const int last = (U.len + kPageSize - 1) / kPageSize - 1;
+            id.i0 = ld_uniform(btr + min(2 * k, last));
+            id.i1 = ld_uniform(btr + min(2 * k + 1, last));
+            id.i2 = id.i0;
+            id.i3 = id.i1;
+        } else if (k < n8) {
+            id.i0 = min(2 * k, a.int8_tiles - 1);
+            id.i1 = min(2 * k + 1, a.int8_tiles - 1);
+            id.i2 = id.i0;
+            id.i3 = id.i1;
+        } else {
+            const int p_first = a.sinks / kPageSize + kInt4StepPages * (k - n8);
+            const int last = p1 - 1;
+            id.i0 = ld_uniform(btr + min(p_first, last));
+            id.i1 = ld_uniform(btr + min(p_first + 1, last));
+            id.i2 = ld_uniform(btr + min(p_first + 2, last));
+            id.i3 = ld_uniform(btr + min(p_first + 3, last));
         }
+        return id;
     }
 
-    // QK + softmax + exchange; returns the PV A operands
-    __device__ __forceinline__ void int4_qk(const DecodeUnit& U, int p_first, int p_end, const Int4Data& dd,
-                                            half4_t& Ahi, half4_t& Alo)
+    // The step's 14 vector loads.  Both step types read four blocks of 16D + 128 bytes shaped
+    // alike: INT4 = the 4 pages; INT8 = block j / 2 of tile j % 2 (tile half j / 2 of the dims for
+    // K, slots 16 (j % 2) + 8 (j / 2) .. +7 for V).  Only the four block addresses differ, so the
+    // loads are the same instructions for both.
+    __device__ __forceinline__ void load_step(const DecodeUnit& U, int k, const Ids& id, Buf& b) const
     {
-        const int npg = min(kInt4StepPages, p_end - p_first);
+        const bool t8 = is_int8_step(k);
+        const uint8_t* base;
+        int64_t stride;
+        if (FMT == FMT_INT4_PROT && t8) {
+            base = a.int8_pool + ((int64_t)U.seq * a.hkv + U.head) * a.int8_tiles * a.int8_tile;
+            stride = a.int8_tile;
+        } else {
+            base = a.pool + (int64_t)U.head * a.page_block;
+            stride = (int64_t)a.hkv * a.page_block;
+        }
+        const int64_t hb = t8 ? (int64_t)(16 * D + 128) : 0;
+        const uint8_t* pg0 = base + (int64_t)id.i0 * stride;
+        const uint8_t* pg1 = base + (int64_t)id.i1 * stride;
+        const uint8_t* pg2 = base + (int64_t)id.i2 * stride + hb;
+        const uint8_t* pg3 = base + (int64_t)id.i3 * stride + hb;
+        // K and scales: slot lane % 16 of block lane / 16
+        const int kb = lane >> 4;
+        const uint8_t* pk = kb == 0 ? pg0 : kb == 1 ? pg1 : kb == 2 ? pg2 : pg3;
+        const uint32_t t16 = (uint32_t)(lane & 15);
+        // one fixed issue order (K, scales, V) everywhere, so that the wait counts agree on every
+        // path into the pipeline loop
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int c2 = 0; c2 < NK; c2++) b.k[c2] = *(const u32x4*)(pk + t16 * 16 + c2 * 256);
+        b.sz = *(const u32x2*)(pk + 16 * D + t16 * 8);
+        // V: dim 64 hv + lane of block q
+#pragma unroll
+        for (int hv = 0; hv < NHV; hv++) {
+            const uint32_t vo = 8 * D + 512 * hv + (uint32_t)lane * 8u;
+            b.v[0 * NHV + hv] = *(const u32x2*)(pg0 + vo);
+            b.v[1 * NHV + hv] = *(const u32x2*)(pg1 + vo);
+            b.v[2 * NHV + hv] = *(const u32x2*)(pg2 + vo);
+            b.v[3 * NHV + hv] = *(const u32x2*)(pg3 + vo);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // ================================ INT4 steps ================================
+    // QK + softmax + exchange; returns the PV A operands
+    __device__ __forceinline__ void int4_qk(const DecodeUnit& U, int k, int p1, const Buf& b, half4_t& Ahi,
+                                            half4_t& Alo)
+    {
+        const int p_first = a.sinks / kPageSize + kInt4StepPages * (k - n8);
+        const int npg = min(kInt4StepPages, p1 - p_first);
         const int pj = lane >> 4, t16 = lane & 15;
         const int pos = (p_first + pj) * kPageSize + t16;
         const bool valid = pj < npg && pos >= a.sinks && pos < U.len - a.recent;
@@ -352,11 +414,11 @@ struct DecodeWave {
         // steps m = 16c + 4wd + 2gp + hl; two accumulation chains
         float4_t S2[2];
         S2[0] = S2[1] = (float4_t){0.f, 0.f, 0.f, 0.f};
-        static_for<0, D / 32>([&](auto C) {
+        static_for<0, NK>([&](auto C) {
             static_for<0, 4>([&](auto WD) {
-                const uint32_t w = dd.kc[C][(int)WD];
-                const uint32_t w8 = w >> 8;
-                const half4_t B0 = to_half4(w & 0x000F000Fu, w & 0x00F000F0u);
+                const uint32_t wv = b.k[C][(int)WD];
+                const uint32_t w8 = wv >> 8;
+                const half4_t B0 = to_half4(wv & 0x000F000Fu, wv & 0x00F000F0u);
                 const half4_t B1 = to_half4(w8 & 0x000F000Fu, w8 & 0x00F000F0u);
                 constexpr int m0 = (4 * C + WD) * 4;
                 constexpr int ch = WD & 1;
@@ -368,8 +430,8 @@ struct DecodeWave {
         });
         const float4_t S = S2[0] + S2[1];
 
-        const float sK = f16_bits_to_float(dd.sz.x & 0xFFFFu), zK = f16_bits_to_float(dd.sz.x >> 16);
-        const float sV = f16_bits_to_float(dd.sz.y & 0xFFFFu), zV = f16_bits_to_float(dd.sz.y >> 16);
+        const float sK = f16_bits_to_float(b.sz.x & 0xFFFFu), zK = f16_bits_to_float(b.sz.x >> 16);
+        const float sV = f16_bits_to_float(b.sz.y & 0xFFFFu), zV = f16_bits_to_float(b.sz.y >> 16);
         const float sK24 = sK * 16777216.0f;
         float sc[4];
 #pragma unroll
@@ -385,15 +447,15 @@ struct DecodeWave {
         exchange_h(pt, st_w, kk, true, true, Ahi, Alo);
     }
 
-    __device__ __forceinline__ void int4_pv(const Int4Data& dd, const half4_t& Ahi, const half4_t& Alo)
+    __device__ __forceinline__ void int4_pv(const Buf& b, const half4_t& Ahi, const half4_t& Alo)
     {
         // pages past the range carry zero probabilities: their (duplicated) codes add nothing
         static_for<0, kInt4StepPages>([&](auto PJ) {
             static_for<0, 2>([&](auto WD) {
                 static_for<0, NHV>([&](auto HV) {
-                    const uint32_t w = dd.vc[PJ][HV][(int)WD];
-                    const uint32_t w8 = w >> 8;
-                    const half4_t B0 = to_half4(w & 0x000F000Fu, w & 0x00F000F0u);
+                    const uint32_t wv = b.v[PJ * NHV + HV][(int)WD];
+                    const uint32_t w8 = wv >> 8;
+                    const half4_t B0 = to_half4(wv & 0x000F000Fu, wv & 0x00F000F0u);
                     const half4_t B1 = to_half4(w8 & 0x000F000Fu, w8 & 0x00F000F0u);
                     constexpr int s0 = PJ * 4 + WD * 2;
                     acc[HV][WD] = mfma_h<s0>(Ahi, B0, acc[HV][WD]);
@@ -406,46 +468,13 @@ struct DecodeWave {
     }
 
     // ================================ INT8 steps ================================
-    // Tile bases of INT8 step j (clamped to existing tiles / pages).
-    __device__ __forceinline__ void int8_bases(const DecodeUnit& U, int j, const uint8_t* (&tb)[2])
-    {
-        if constexpr (FMT == FMT_INT4_PROT) {
-            const uint8_t* seg = a.int8_pool + ((int64_t)U.seq * a.hkv + U.head) * a.int8_tiles * a.int8_tile;
-#pragma unroll
-            for (int tt = 0; tt < 2; tt++) tb[tt] = seg + (int64_t)min(2 * j + tt, a.int8_tiles - 1) * a.int8_tile;
-        } else {
-            const int npages = (U.len + kPageSize - 1) / kPageSize;
-            const int32_t* btr = a.bt + (int64_t)U.seq * a.max_pps;
-#pragma unroll
-            for (int tt = 0; tt < 2; tt++)
-                tb[tt] = a.pool + (int64_t)ld_uniform(btr + min(2 * j + tt, npages - 1)) * a.hkv * a.page_block +
-                         (int64_t)U.head * a.page_block;
-        }
-    }
-
-    __device__ __forceinline__ void int8_load(const uint8_t* const (&tb)[2], Int8Data& dd)
-    {
-        const int sl = lane & 31;
-        // per-lane offset from tile 0 (keeps the access a global-memory load)
-        const int64_t d01 = tb[1] - tb[0];
-        const uint8_t* t = tb[0] + ((sl >> 4) ? d01 : (int64_t)0);
-        const int s8 = sl & 15;
-#pragma unroll
-        for (int c = 0; c < D / 16; c++) dd.k8[c] = *(const u32x4*)(t + c * 256 + s8 * 16);
-        dd.sz = *(const u32x2*)(t + 32 * D + s8 * 8);
-#pragma unroll
-        for (int tt = 0; tt < 2; tt++)
-#pragma unroll
-            for (int hv = 0; hv < NHV; hv++) dd.v8[tt][hv] = *(const u32x4*)(tb[tt] + 16 * D + (64 * hv + lane) * 16);
-    }
-
-    __device__ __forceinline__ void int8_compute(const DecodeUnit& U, int j, const Int8Data& dd)
+    __device__ __forceinline__ void int8_qk(const DecodeUnit& U, int k, const Buf& b, half4_t& Ahi, half4_t& Alo)
     {
         const bool lane_ok = lane < 32;
         const int sl = lane & 31;
         bool valid = false;
         if constexpr (FMT == FMT_INT4_PROT) {
-            const int u = kInt8StepSlots * j + sl;
+            const int u = kInt8StepSlots * k + sl;
             const int L = U.len;
             if (lane_ok && u < a.sinks + a.recent) {
                 if (u < a.sinks) {
@@ -456,28 +485,30 @@ struct DecodeWave {
                 }
             }
         } else {
-            const int pos = (2 * j + (sl >> 4)) * kPageSize + (sl & 15);
+            const int pos = (2 * k + (sl >> 4)) * kPageSize + (sl & 15);
             valid = lane_ok && pos < U.len;
         }
 
-        // QK: word (c, wd) holds dims 4u..4u+3 (u = 4c + wd); steps m = 2u + hl
+        // QK over the lane's half of the dims: word (c, wd) holds dims h*D/2 + 4u .. +3 with
+        // u = 4c + wd; steps m = 2u + hl use pair c, block 2wd + hl of the half
         float4_t S4[4];
 #pragma unroll
-        for (int c = 0; c < 4; c++) S4[c] = (float4_t){0.f, 0.f, 0.f, 0.f};
-        static_for<0, D / 16>([&](auto C) {
+        for (int q = 0; q < 4; q++) S4[q] = (float4_t){0.f, 0.f, 0.f, 0.f};
+        static_for<0, NK>([&](auto C) {
             static_for<0, 4>([&](auto WD) {
-                const uint32_t w = dd.k8[C][(int)WD];
-                const half4_t B = to_half4(__builtin_amdgcn_perm(0u, w, 0x0C010C00u),
-                                           __builtin_amdgcn_perm(0u, w, 0x0C030C02u));
-                constexpr int u = 4 * C + WD;
-                S4[WD] = mfma_h<(2 * u) % 16>(A8[(2 * u) / 16], B, S4[WD]);
-                S4[WD] = mfma_h<(2 * u + 1) % 16>(A8[(2 * u + 1) / 16], B, S4[WD]);
+                const uint32_t wv = b.k[C][(int)WD];
+                const half4_t B = to_half4(__builtin_amdgcn_perm(0u, wv, 0x0C010C00u),
+                                           __builtin_amdgcn_perm(0u, wv, 0x0C030C02u));
+                S4[WD] = mfma_h_half<2 * WD>(A8[C], B, S4[WD]);
+                S4[WD] = mfma_h_half<2 * WD + 1>(A8[C], B, S4[WD]);
             });
         });
-        const float4_t S = (S4[0] + S4[1]) + (S4[2] + S4[3]);
+        float4_t S = (S4[0] + S4[1]) + (S4[2] + S4[3]);
+#pragma unroll
+        for (int i = 0; i < 4; i++) S[i] = S[i] + __shfl_xor(S[i], 32, 64);
 
-        const float sK = f16_bits_to_float(dd.sz.x & 0xFFFFu), zK = f16_bits_to_float(dd.sz.x >> 16);
-        const float sV = f16_bits_to_float(dd.sz.y & 0xFFFFu), zV = f16_bits_to_float(dd.sz.y >> 16);
+        const float sK = f16_bits_to_float(b.sz.x & 0xFFFFu), zK = f16_bits_to_float(b.sz.x >> 16);
+        const float sV = f16_bits_to_float(b.sz.y & 0xFFFFu), zV = f16_bits_to_float(b.sz.y >> 16);
         const float sK24 = sK * 16777216.0f;
         float sc[4];
 #pragma unroll
@@ -485,23 +516,110 @@ struct DecodeWave {
         const float lg = (sV > 0.f) ? __builtin_amdgcn_logf(sV) : -24.f;
         float pt[4];
         softmax_step(sc, lg, valid, valid ? sV : 0.f, valid ? zV : 0.f, pt);
-
-        half4_t Ahi, Alo;
         exchange_h(pt, sl >> 2, sl & 3, lane_ok, false, Ahi, Alo);
+    }
 
-        // tiles past the range carry zero probabilities
-        static_for<0, 2>([&](auto TT) {
-            static_for<0, 4>([&](auto Q) {
+    __device__ __forceinline__ void int8_pv(const Buf& b, const half4_t& Ahi, const half4_t& Alo)
+    {
+        // v[q * NHV + hv] word w holds slots 16 (q % 2) + 8 (q / 2) + 4 w .. +3 of dim 64 hv + lane:
+        // PV step 4 (q % 2) + 2 (q / 2) + w.  Tiles past the range carry zero probabilities.
+        static_for<0, 4>([&](auto Q) {
+            static_for<0, 2>([&](auto WW) {
                 static_for<0, NHV>([&](auto HV) {
-                    const uint32_t w = dd.v8[TT][HV][(int)Q];
-                    const half4_t B = to_half4(__builtin_amdgcn_perm(0u, w, 0x0C010C00u),
-                                               __builtin_amdgcn_perm(0u, w, 0x0C030C02u));
-                    constexpr int s0 = 4 * TT + Q;
-                    acc[HV][TT] = mfma_h<s0>(Ahi, B, acc[HV][TT]);
-                    acc[HV][TT] = mfma_h<s0>(Alo, B, acc[HV][TT]);
+                    const uint32_t wv = b.v[Q * NHV + HV][(int)WW];
+                    const half4_t B = to_half4(__builtin_amdgcn_perm(0u, wv, 0x0C010C00u),
+                                               __builtin_amdgcn_perm(0u, wv, 0x0C030C02u));
+                    constexpr int s0 = 4 * (Q % 2) + 2 * (Q / 2) + WW;
+                    acc[HV][Q % 2] = mfma_h<s0>(Ahi, B, acc[HV][Q % 2]);
+                    acc[HV][Q % 2] = mfma_h<s0>(Alo, B, acc[HV][Q % 2]);
                 });
             });
         });
+    }
+
+    // arithmetic of step k on buffer b
+    __device__ __forceinline__ void compute_qk(const DecodeUnit& U, int k, int p1, const Buf& b, half4_t& Ahi,
+                                               half4_t& Alo)
+    {
+        if (is_int8_step(k))
+            int8_qk(U, k, b, Ahi, Alo);
+        else
+            int4_qk(U, k, p1, b, Ahi, Alo);
+    }
+
+    __device__ __forceinline__ void compute_pv(int k, const Buf& b, const half4_t& Ahi, const half4_t& Alo)
+    {
+        if (is_int8_step(k))
+            int8_pv(b, Ahi, Alo);
+        else
+            int4_pv(b, Ahi, Alo);
+    }
+
+    // ---- one unit's steps [k0, k1) (quantized formats): INT8 and INT4 steps in one pipeline ----
+    __device__ void run_unit(const DecodeUnit& U, int k0, int k1)
+    {
+        const int p1 = (FMT == FMT_INT4_PROT) ? int4_p1(U.len) : 0;
+        Ids id = step_ids(U, k0, p1);
+        // query rows of the unit (issued first: the prologue waits for them only): lane l holds
+        // 8 bf16 of head l / (D/8), dims 8 (l % (D/8)) .. +7
+        const uint16_t* pq = a.q + ((int64_t)U.entry * (a.hkv * G) + U.head * G) * D + 8 * min(lane, QLANES - 1);
+        const u32x4 qraw = *(const u32x4*)pq;
+        Buf A, B;
+        load_step(U, k0, id, A);
+        id = step_ids(U, min(k0 + 1, k1 - 1), p1);
+        prologue_q(qraw);
+        int k = k0;
+        while (true) {
+            half4_t Ahi, Alo;
+            load_step(U, min(k + 1, k1 - 1), id, B); // step k + 1 (or step k again at the end: cached lines)
+            compute_qk(U, k, p1, A, Ahi, Alo);
+            id = step_ids(U, min(k + 2, k1 - 1), p1);
+            compute_pv(k, A, Ahi, Alo);
+            if (++k >= k1) break;
+            load_step(U, min(k + 1, k1 - 1), id, A);
+            compute_qk(U, k, p1, B, Ahi, Alo);
+            id = step_ids(U, min(k + 2, k1 - 1), p1);
+            compute_pv(k, B, Ahi, Alo);
+            if (++k >= k1) break;
+        }
+    }
+
+    // ---- the wave's steps [s, s_end), starting in unit u (quantized formats) ----
+    __device__ void run(int u, int64_t s)
+    {
+        while (s < s_end) {
+            const DecodeUnit U = ld_unit(a.units, u);
+            const int64_t ue = (u + 1 < a.n_units) ? ld_uniform(&a.units[u + 1].step_begin) : a.total_steps;
+            const int k0 = (int)(s - U.step_begin);
+            const int k1 = (int)((s_end < ue ? s_end : ue) - U.step_begin);
+            run_unit(U, k0, k1);
+            epilogue(w + u);
+            s = U.step_begin + k1;
+            u++;
+        }
+        wait_vm_all();
+    }
+
+    // ================================ BF16 baseline ================================
+    // q: lane (4 s + i) holds dims 4m..4m+3 of head i for A step m = 16 v + s, pair v
+    __device__ __forceinline__ void prologue_bf16(const DecodeUnit& U)
+    {
+        reset_state();
+        const uint16_t* qrow = a.q + ((int64_t)U.entry * (a.hkv * G) + U.head * G) * D;
+        const int s = lane >> 2, i = lane & 3;
+        const bool live = i < G;
+        const int ic = live ? i : 0;
+#pragma unroll
+        for (int v = 0; v < NPAIR_BF; v++) {
+            const uint32_t* src = (const uint32_t*)(qrow + ic * D + 4 * (16 * v + s));
+            const uint32_t lo = src[0], hi = src[1];
+            Abf[v] = to_short4(live ? lo : 0u, live ? hi : 0u);
+        }
+#pragma unroll
+        for (int i2 = 0; i2 < 4; i2++) {
+            F[i2] = a.scale_log2;
+            sumq[i2] = 0.f;
+        }
     }
 
     // ================================ BF16 steps ================================
@@ -602,77 +720,25 @@ struct DecodeWave {
         }
     }
 
-    // ---- one unit's steps [k0, k1) ----
-    __device__ void run_unit(const DecodeUnit& U, int k0, int k1)
+    // ---- the wave's steps [s, s_end) for the BF16 format (one page per step, no prefetch) ----
+    __device__ void run_bf16(int u, int64_t s)
     {
-        uint32_t qr[NQ];
-        load_q(U, qr);
-        if constexpr (FMT == FMT_BF16) {
-            prologue(qr, false, false);
+        while (s < s_end) {
+            const DecodeUnit U = ld_unit(a.units, u);
+            const int64_t ue = (u + 1 < a.n_units) ? ld_uniform(&a.units[u + 1].step_begin) : a.total_steps;
+            const int k0 = (int)(s - U.step_begin);
+            const int k1 = (int)((s_end < ue ? s_end : ue) - U.step_begin);
+            prologue_bf16(U);
             for (int k = k0; k < k1; k++) bf16_step(U, k);
-            return;
-        } else {
-            int n8 = 0, p0 = 0, p1 = 0;
-            if constexpr (FMT == FMT_INT4_PROT) {
-                n8 = (a.sinks + a.recent > 0) ? (a.sinks + a.recent + kInt8StepSlots - 1) / kInt8StepSlots : 0;
-                const int lo4 = a.sinks, hi4 = U.len - a.recent;
-                if (hi4 > lo4) {
-                    p0 = lo4 / kPageSize;
-                    p1 = (hi4 - 1) / kPageSize + 1;
-                }
-            } else {
-                n8 = k1; // every step of the INT8 format is an INT8 step
-            }
-            const int e8 = min(k1, n8); // INT8 steps are [k0, e8), INT4 steps [max(k0, n8), k1)
-            int k = k0;
-            Int4Data a4, b4;
-            int32_t ida[4], idb[4];
-            if (k < e8) {
-                // INT8 steps (a few per unit in the INT4 format): one buffer, no prefetch
-                Int8Data a8;
-                const uint8_t* tba[2];
-                int8_bases(U, k, tba);
-                int8_load(tba, a8);
-                prologue(qr, k1 > n8, true);
-                while (true) {
-                    int8_compute(U, k, a8);
-                    if (++k >= e8) break;
-                    int8_bases(U, k, tba);
-                    int8_load(tba, a8);
-                }
-                if (k >= k1) return;
-                int4_ids(U, p0, p1, ida);
-                int4_load(U, ida, a4);
-            } else {
-                int4_ids(U, p0 + kInt4StepPages * (k - n8), p1, ida);
-                int4_load(U, ida, a4);
-                prologue(qr, true, false);
-            }
-            // INT4 steps [k, k1): ping-pong; page ids one step ahead of the data
-            int kn = min(k + 1, k1 - 1);
-            int4_ids(U, p0 + kInt4StepPages * (kn - n8), p1, idb);
-            while (true) {
-                half4_t Ahi, Alo;
-                int4_load(U, idb, b4); // step k + 1 (or step k again at the end: cached lines)
-                int4_qk(U, p0 + kInt4StepPages * (k - n8), p1, a4, Ahi, Alo);
-                kn = min(k + 2, k1 - 1);
-                int4_ids(U, p0 + kInt4StepPages * (kn - n8), p1, ida);
-                int4_pv(a4, Ahi, Alo);
-                if (++k >= k1) break;
-                int4_load(U, ida, a4);
-                int4_qk(U, p0 + kInt4StepPages * (k - n8), p1, b4, Ahi, Alo);
-                kn = min(k + 2, k1 - 1);
-                int4_ids(U, p0 + kInt4StepPages * (kn - n8), p1, idb);
-                int4_pv(b4, Ahi, Alo);
-                if (++k >= k1) break;
-            }
-            wait_vm_all();
+            epilogue(w + u);
+            s = U.step_begin + k1;
+            u++;
         }
     }
 };
 
 template <int D, int G, int FMT>
-__global__ __launch_bounds__(64 * kWavesPerBlock) __attribute__((amdgpu_waves_per_eu(3)))
+__global__ __launch_bounds__(64 * kWavesPerBlock) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_split_kernel(DecodeArgs a)
 {
     __shared__ __align__(16) uint8_t lds_all[kWavesPerBlock][kLdsPerWave];
@@ -681,7 +747,7 @@ void decode_split_kernel(DecodeArgs a)
     const int64_t w = (int64_t)blockIdx.x * kWavesPerBlock + wv;
     if (w >= a.n_waves) return;
     const int64_t T = a.total_steps, W = a.n_waves;
-    int64_t s = w * T / W;
+    const int64_t s = w * T / W;
     const int64_t s_end = (w + 1) * T / W;
     if (s >= s_end) return;
     int lo = 0, hi = a.n_units - 1;
@@ -692,18 +758,11 @@ void decode_split_kernel(DecodeArgs a)
         else
             hi = mid - 1;
     }
-    int u = lo;
-    DecodeWave<D, G, FMT> dw(a, lane, lds_all[wv], lds_all[wv] + kLdsQBytes);
-    while (s < s_end) {
-        const DecodeUnit U = ld_unit(a.units, u);
-        const int64_t ue = (u + 1 < a.n_units) ? ld_uniform(&a.units[u + 1].step_begin) : T;
-        const int k0 = (int)(s - U.step_begin);
-        const int k1 = (int)((s_end < ue ? s_end : ue) - U.step_begin);
-        dw.run_unit(U, k0, k1);
-        dw.epilogue(w + u);
-        s = U.step_begin + k1;
-        u++;
-    }
+    DecodeWave<D, G, FMT> dw(a, lane, lds_all[wv], lds_all[wv] + kLdsQBytes, w, s_end);
+    if constexpr (FMT == FMT_BF16)
+        dw.run_bf16(lo, s);
+    else
+        dw.run(lo, s);
 }
 
 // ---------------------------------------------------------------------------------------------

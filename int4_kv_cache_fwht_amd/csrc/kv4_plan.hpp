@@ -69,7 +69,7 @@ inline Sizes buffer_sizes(const Config& c)
 {
     Sizes s;
     size_t D = (size_t)c.d;
-    s.int8_tile = 32 * D + 128;
+    s.int8_tile = 2 * (16 * D + 128); // two blocks shaped like an INT4 page block
     if (c.format == FMT_INT4_PROT)
         s.page_block = 16 * D + 128;
     else if (c.format == FMT_INT8)

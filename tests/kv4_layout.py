@@ -29,15 +29,24 @@ def int4_page_block(block: np.ndarray, D: int):
 
 
 def int8_tile(block: np.ndarray, D: int):
-    """One INT8 tile (protection slots or INT8-format page) -> codes [16][2][D], scales [16][2][2]."""
-    assert block.dtype == np.uint8 and block.size == 32 * D + 128
+    """One INT8 tile (protection slots or INT8-format page) -> codes [16][2][D], scales [16][2][2].
+
+    The tile is two blocks of 16D + 128 bytes.  Block x holds K dims x*D/2 .. (x+1)*D/2 - 1 of
+    all 16 slots as [D/32 chunks][16 slots][16 B] (one byte per dim), V of slots 8x .. 8x+7 as
+    [D dims][8 B] (byte j = slot 8x + j), and the scales [16][4 x fp16].  Both blocks carry the
+    same scales; the second copy is returned as a third output for comparison."""
+    bb = 16 * D + 128
+    assert block.dtype == np.uint8 and block.size == 2 * bb
     codes = np.zeros((P, 2, D), dtype=np.uint8)
-    k = block[: 16 * D].reshape(D // 16, P, 16)        # [c][t][16 dims]
-    codes[:, 0, :] = k.transpose(1, 0, 2).reshape(P, D)
-    v = block[16 * D: 32 * D].reshape(D, P)             # [d][slot]
-    codes[:, 1, :] = v.T
-    sz = block[32 * D: 32 * D + 128].view(np.uint16).reshape(P, 2, 2)
-    return codes, sz
+    sz = []
+    for x in range(2):
+        b = block[x * bb:(x + 1) * bb]
+        k = b[: 8 * D].reshape(D // 32, P, 16)                # [c][t][16 dims]
+        codes[:, 0, x * D // 2:(x + 1) * D // 2] = k.transpose(1, 0, 2).reshape(P, D // 2)
+        v = b[8 * D: 16 * D].reshape(D, 8)                    # [d][slot 8x + j]
+        codes[8 * x: 8 * x + 8, 1, :] = v.T
+        sz.append(b[16 * D: 16 * D + 128].view(np.uint16).reshape(P, 2, 2))
+    return codes, sz[0], sz[1]
 
 
 def bf16_page_block(block: np.ndarray, D: int):

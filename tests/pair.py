@@ -63,7 +63,8 @@ class Pair:
                     if self.fmt == kv4.FORMAT_INT4_PROT:
                         gc, gs = kv4_layout.int4_page_block(blk, self.d)
                     elif self.fmt == kv4.FORMAT_INT8:
-                        gc, gs = kv4_layout.int8_tile(blk, self.d)
+                        gc, gs, gs2 = kv4_layout.int8_tile(blk, self.d)
+                        assert (gs2[:nv] == gs[:nv]).all(), ("second scale copy", s, j, h)
                     else:
                         gc, gs = kv4_layout.bf16_page_block(blk, self.d), None
                     bad = np.argwhere(gc[:nv] != odata[:nv])
@@ -76,12 +77,13 @@ class Pair:
             if i8 is not None:
                 for u in range(self.S + self.R):
                     for h in range(self.hkv):
-                        gc, gs = kv4_layout.int8_tile(i8[s, h, u // 16], self.d)
+                        gc, gs, gs2 = kv4_layout.int8_tile(i8[s, h, u // 16], self.d)
                         for kv in range(2):
                             oc, (os_, oz), tok = self.ora.int8_slot_contents(s, u, h, kv)
                             if tok < 0 or not oracle.is_protected(tok, L, self.S, self.R):
                                 continue
                             assert (gc[u % 16, kv] == oc).all(), ("int8 codes", s, u, h, kv)
                             assert gs[u % 16, kv, 0] == os_ and gs[u % 16, kv, 1] == oz, ("int8 scales", s, u, h, kv)
+                            assert (gs2[u % 16, kv] == gs[u % 16, kv]).all(), ("int8 second scale copy", s, u, h, kv)
                             compared += 1
         return compared

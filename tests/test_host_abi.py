@@ -67,9 +67,10 @@ def test_status_strings(libkv4):
 
 def _documented_sizes(hq, hkv, d, num_pages, max_seqs, max_pps, S, R, fmt):
     """Sizes from the layout the header documents: an INT4 page block is 16 slots x (D/2 bytes of K
-    codes + D/2 of V codes + 4 fp16 scale/zero) ; an INT8 tile 16 x (D + D + 8); a bf16 page 16 x 2D
-    bf16; INT8 protection tiles per (sequence, kv head) = ceil((S + R) / 16)."""
-    int8_tile = 16 * (d + d + 8)
+    codes + D/2 of V codes + 4 fp16 scale/zero); an INT8 tile is two such-shaped blocks (D/2 bytes of
+    K + 8 slots x D bytes of V ... per block, scales in both); a bf16 page 16 x 2D bf16; INT8
+    protection tiles per (sequence, kv head) = ceil((S + R) / 16)."""
+    int8_tile = 2 * (16 * (d // 2 + d // 2 + 8))
     if fmt == 0:
         block = 16 * (d // 2 + d // 2 + 8)
     elif fmt == 1:
