@@ -864,6 +864,27 @@ hipError_t launch_decode_split(int d, int g, int format, const DecodeArgs& a, hi
     KV4_DEC_DISPATCH(launch_split_t)
 }
 
+template <int D, int G, int F>
+static hipError_t residency_t(int* blocks_per_cu)
+{
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, decode_split_kernel<D, G, F>,
+                                                        64 * kWavesPerBlock, 0);
+}
+
+hipError_t decode_split_residency(int d, int g, int format, int* blocks_per_cu)
+{
+#define KV4_RES_CASE(DD, GG, FF) \
+    if (d == DD && g == GG && format == FF) return residency_t<DD, GG, FF>(blocks_per_cu);
+    KV4_RES_CASE(64, 1, 0) KV4_RES_CASE(64, 2, 0) KV4_RES_CASE(64, 4, 0)
+    KV4_RES_CASE(64, 1, 1) KV4_RES_CASE(64, 2, 1) KV4_RES_CASE(64, 4, 1)
+    KV4_RES_CASE(64, 1, 2) KV4_RES_CASE(64, 2, 2) KV4_RES_CASE(64, 4, 2)
+    KV4_RES_CASE(128, 1, 0) KV4_RES_CASE(128, 2, 0) KV4_RES_CASE(128, 4, 0)
+    KV4_RES_CASE(128, 1, 1) KV4_RES_CASE(128, 2, 1) KV4_RES_CASE(128, 4, 1)
+    KV4_RES_CASE(128, 1, 2) KV4_RES_CASE(128, 2, 2) KV4_RES_CASE(128, 4, 2)
+#undef KV4_RES_CASE
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_decode_merge(int d, int g, int format, const DecodeArgs& a, hipStream_t stream)
 {
     KV4_DEC_DISPATCH(launch_merge_t)

@@ -146,6 +146,7 @@ struct kv4_cache {
     kv4_buffers bufs{};
     int device = 0;
     int num_cus = 256;
+    int resident_waves = 2048; // decode split waves resident at once on the device
     int decode_waves = 0; // 0: automatic
     float cb = 1.0f;
     Staging staging;
@@ -206,11 +207,20 @@ struct DeviceGuard {
     }
 };
 
-int auto_waves(const kv4_cache* h) { return h->num_cus * 8; }
+// Decode split waves: one full round of resident waves, or two rounds when every wave would
+// otherwise get many steps (the second round then evens out the tail).  A partial extra round is
+// never used: its waves would finish late.
+constexpr int64_t kStepsForTwoRounds = 32;
 
-int max_waves(const kv4_cache* h)
+int64_t auto_waves(const kv4_cache* h, int64_t total_steps)
 {
-    int w = auto_waves(h);
+    const int64_t cap = h->resident_waves;
+    return total_steps >= kStepsForTwoRounds * cap ? 2 * cap : cap;
+}
+
+int64_t max_waves(const kv4_cache* h)
+{
+    int64_t w = 2 * (int64_t)h->resident_waves;
     if (h->decode_waves > w) w = h->decode_waves;
     return w;
 }
@@ -295,6 +305,15 @@ kv4_status kv4_cache_create(const kv4_config* cfg, const kv4_buffers* bufs, kv4_
     h->bufs = *bufs;
     h->device = dev;
     h->num_cus = cus > 0 ? cus : 256;
+    {
+        int bpc = 0;
+        e = kv4::decode_split_residency(c.d, c.hq / c.hkv, c.format, &bpc);
+        if (e != hipSuccess) {
+            delete h;
+            return hip_fail(nullptr, e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+        }
+        h->resident_waves = (bpc > 0 ? bpc : 1) * kv4::kWavesPerBlock * h->num_cus;
+    }
     h->cb = (float)(1.0 / std::sqrt((double)c.block));
     e = h->staging.init(8);
     if (e != hipSuccess) {
@@ -423,7 +442,7 @@ kv4_status kv4_decode_attention(kv4_cache_t h, int32_t n_seqs, const int32_t* se
     if (s != kv4::OK) return fail(h, (kv4_status)s, msg);
     if (units.empty()) return KV4_OK;
     const int64_t wmax = max_waves(h);
-    int64_t W = h->decode_waves > 0 ? h->decode_waves : auto_waves(h);
+    int64_t W = h->decode_waves > 0 ? h->decode_waves : auto_waves(h, total);
     if (W > total) W = total;
     if (W < 1) W = 1;
     const int64_t n_units = (int64_t)units.size();

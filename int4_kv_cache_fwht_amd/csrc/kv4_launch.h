@@ -42,5 +42,7 @@ struct DecodeArgs {
 hipError_t launch_append(int d, int format, int n_tasks, const AppendArgs& a, hipStream_t stream);
 hipError_t launch_decode_split(int d, int g, int format, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_merge(int d, int g, int format, const DecodeArgs& a, hipStream_t stream);
+// Workgroups of the split kernel (4 waves each) that fit on one compute unit at once.
+hipError_t decode_split_residency(int d, int g, int format, int* blocks_per_cu);
 
 } // namespace kv4
