@@ -766,7 +766,9 @@ void decode_split_kernel(DecodeArgs a)
 }
 
 // ---------------------------------------------------------------------------------------------
-// merge: one block of G x D threads per unit; thread (i, d) merges head i, dim d
+// merge: one wave per (unit, q head) -- lane holds dims lane + 64 j -- combines the unit's partials
+// in wave order (log-sum-exp against their common maximum), then applies the inverse rotation
+// (H is symmetric: the same FWHT and the fl32(1/sqrt(b)) scale) in registers
 // ---------------------------------------------------------------------------------------------
 
 __device__ __forceinline__ int64_t wave_of_step(int64_t step, int64_t T, int64_t W)
@@ -776,46 +778,61 @@ __device__ __forceinline__ int64_t wave_of_step(int64_t step, int64_t T, int64_t
 }
 
 template <int D, int G, bool ROT>
-__global__ __launch_bounds__(G * D) void merge_kernel(DecodeArgs a)
+__global__ __launch_bounds__(64 * G) void merge_kernel(DecodeArgs a)
 {
-    __shared__ float buf[G * D];
+    constexpr int NHV = D / 64;
     const int u = blockIdx.x;
-    const int i = threadIdx.x / D, d = threadIdx.x % D;
+    const int i = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
     const DecodeUnit U = ld_unit(a.units, u);
     const int64_t T = a.total_steps, W = a.n_waves;
     const int64_t sb = U.step_begin;
     const int64_t se = (u + 1 < a.n_units) ? ld_uniform(&a.units[u + 1].step_begin) : T;
     const int64_t w0 = wave_of_step(sb, T, W), w1 = wave_of_step(se - 1, T, W);
     const int n = (int)(w1 - w0 + 1);
+    // partial j of this unit sits at index w0 + u + j; (m, l) are read with scalar loads (the split
+    // kernel that wrote them has completed)
     const float* ml = a.part_ml + ((w0 + u) * G + i) * 2;
-    const float* po = a.part_o + ((w0 + u) * G + i) * D + d;
+    const float* po = a.part_o + ((w0 + u) * G + i) * D + lane;
     float M = -INFINITY;
-    for (int j = 0; j < n; j++) M = fmaxf(M, ml[(int64_t)j * G * 2]);
-    float Ls = 0.f, O = 0.f;
+    for (int j = 0; j < n; j++) M = fmaxf(M, ld_uniform(ml + (int64_t)j * G * 2));
+    float Ls = 0.f, O[NHV];
+#pragma unroll
+    for (int hv = 0; hv < NHV; hv++) O[hv] = 0.f;
     if (M != -INFINITY) {
-#pragma unroll 4
+#pragma unroll 16
         for (int j = 0; j < n; j++) {
-            const float mw = ml[(int64_t)j * G * 2];
+            const float mw = ld_uniform(ml + (int64_t)j * G * 2);
             const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-            Ls = fmaf(ml[(int64_t)j * G * 2 + 1], f, Ls);
-            O = fmaf(po[(int64_t)j * G * D], f, O);
+            Ls = fmaf(ld_uniform(ml + (int64_t)j * G * 2 + 1), f, Ls);
+#pragma unroll
+            for (int hv = 0; hv < NHV; hv++) O[hv] = fmaf(po[(int64_t)j * G * D + 64 * hv], f, O[hv]);
         }
     }
-    float r = (Ls > 0.f) ? O / Ls : 0.f;
+    float r[NHV];
+#pragma unroll
+    for (int hv = 0; hv < NHV; hv++) r[hv] = (Ls > 0.f) ? O[hv] / Ls : 0.f;
     if (ROT && a.block > 1) {
-        float* bh = buf + i * D;
-        bh[d] = r;
-        for (int hh = 1; hh < a.block; hh <<= 1) {
-            __syncthreads();
-            const float other = bh[d ^ hh];
-            const float mine = bh[d];
-            __syncthreads();
-            bh[d] = (d & hh) ? other - mine : mine + other;
+        for (int hh = 1; hh < a.block && hh < 64; hh <<= 1) {
+#pragma unroll
+            for (int hv = 0; hv < NHV; hv++) {
+                const float other = __shfl_xor(r[hv], hh, 64);
+                r[hv] = (lane & hh) ? other - r[hv] : r[hv] + other;
+            }
         }
-        __syncthreads();
-        r = bh[d] * a.cb;
+        if constexpr (NHV > 1) {
+            if (a.block > 64) {
+                const float a0 = r[0], a1 = r[1];
+                r[0] = a0 + a1;
+                r[1] = a0 - a1;
+            }
+        }
+#pragma unroll
+        for (int hv = 0; hv < NHV; hv++) r[hv] = r[hv] * a.cb;
     }
-    a.out[((int64_t)U.entry * (a.hkv * G) + U.head * G + i) * D + d] = r;
+    float* o = a.out + ((int64_t)U.entry * (a.hkv * G) + U.head * G + i) * D + lane;
+#pragma unroll
+    for (int hv = 0; hv < NHV; hv++) o[64 * hv] = r[hv];
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -833,7 +850,7 @@ static hipError_t launch_split_t(const DecodeArgs& a, hipStream_t stream)
 template <int D, int G, int F>
 static hipError_t launch_merge_t(const DecodeArgs& a, hipStream_t stream)
 {
-    hipLaunchKernelGGL((merge_kernel<D, G, F != FMT_BF16>), dim3((unsigned)a.n_units), dim3(G * D), 0, stream, a);
+    hipLaunchKernelGGL((merge_kernel<D, G, F != FMT_BF16>), dim3((unsigned)a.n_units), dim3(64 * G), 0, stream, a);
     return hipGetLastError();
 }
 
