@@ -33,13 +33,16 @@ def parse():
     ap.add_argument("--steps", type=int, default=40)
     ap.add_argument("--warmup", type=int, default=4)
     ap.add_argument("--workload", default="qwen3_8b_layer",
-                    choices=["qwen3_8b_layer", "rollout", "long_context", "tiny"])
+                    choices=["qwen3_8b_layer", "rollout", "long_context", "tiny", "append"],
+                    help="decode workloads, or 'append': the append path alone at Hadamard block 128 vs 1")
     ap.add_argument("--caches", type=int, default=4, help="distinct layer caches cycled (defeats the 256 MB MALL)")
     ap.add_argument("--baselines", default="int8,bf16", help="comma list of baseline formats ('' for none)")
     ap.add_argument("--baseline-steps", type=int, default=12)
     ap.add_argument("--cpu-baseline-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-waves", type=int, default=0)
+    ap.add_argument("--hadamard-block", type=int, default=0,
+                    help="override the workload's Hadamard block (1 = plain INT4: no q / output rotation)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference kernel for PMC byte counters)")
     return ap.parse_args()
@@ -240,6 +243,58 @@ def copy_probe(device):
     return 2 * n * reps / el / 1e9
 
 
+def append_workload(device, repeats=7):
+    """The append path alone: 256 empty sequences x 512 single-position steps, and a bulk prefill of
+    32768 positions into one sequence, timed with the rotation (b = 128) and without it (b = 1,
+    plain INT4).  Returns the JSON record."""
+    import torch
+    import int4_kv_cache_fwht_amd as kv4
+    import kv4_inputs as W
+    w = W.WORKLOADS["append"]
+    hq, hkv, d = w.num_q_heads, w.num_kv_heads, w.head_dim
+    B, steps, bulk = 256, 512, 32768
+    ch = W.outlier_channels(hkv, d, w.outlier_channels, w.seed)
+    rows = [W.seq_kv(hkv, d, B, ch, w.outlier_scale, w.seed, 2000 + s, 0, device) for s in range(steps)]
+    kb, vb = W.seq_kv(hkv, d, bulk, ch, w.outlier_scale, w.seed, 3000, 0, device)
+    res = {}
+    for block in (128, 1):
+        cfg = kv4.Config(num_q_heads=hq, num_kv_heads=hkv, head_dim=d, num_pages=B * (steps // 16) + bulk // 16 + 16,
+                         max_seqs=B + 1, max_pages_per_seq=bulk // 16 + 1, num_sinks=w.num_sinks,
+                         num_recent=w.num_recent, hadamard_block=block, format=0)
+        best_steps = best_bulk = float("inf")
+        for _ in range(repeats):
+            cache = kv4.Cache(cfg, device)
+            ids = list(range(B))
+            cache.append(ids, [1] * B, rows[0][0], rows[0][1])  # warm-up of the launch path
+            torch.cuda.synchronize()
+            cache.seq_free(0)
+            for i in ids[1:]:
+                cache.seq_free(i)
+            cache.profile_enable(True)
+            for s in range(steps):
+                cache.append(ids, [1] * B, rows[s][0], rows[s][1])
+            p = cache.profile_read()
+            best_steps = min(best_steps, p["append_ms"] / p["append_launches"] * 1e3)
+            cache.profile_enable(True)
+            cache.append([B], [bulk], kb, vb)
+            p = cache.profile_read()
+            best_bulk = min(best_bulk, p["append_ms"] * 1e3)
+            cache.profile_enable(False)
+            del cache
+        res[block] = (best_steps, best_bulk)
+    (s128, b128), (s1, b1) = res[128], res[1]
+    bulk_bytes = bulk * hkv * d * 2 * 2 + bulk * hkv * 2 * (d // 2 + 4)   # bf16 in, INT4 + scales out
+    return {"metric": "INT4 KV append (rotation + quantization + pack) tokens/s", "value": B / (s128 * 1e-6),
+            "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": 1, "ms_per_step": s128 * 1e-3,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": "append", "sequences": B, "steps": steps, "bulk_prefill": bulk, "kv_heads": hkv,
+                       "head_dim": d, "sinks": w.num_sinks, "recent": w.num_recent},
+            "append_step_us": {"b128": s128, "b1": s1, "rotation_overhead": s128 / s1 - 1.0},
+            "bulk_prefill_us": {"b128": b128, "b1": b1, "rotation_overhead": b128 / b1 - 1.0,
+                                "GBps_b128": bulk_bytes / (b128 * 1e-6) / 1e9},
+            "note": "best of %d repeats; kernel time from HIP events on the call's stream" % repeats}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -250,7 +305,13 @@ def main():
     import kv4_inputs as W
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     device = torch.device("cuda", 0)
+    if args.workload == "append":
+        print(json.dumps(append_workload(device)), flush=True)
+        return
     w = W.WORKLOADS[args.workload]
+    if args.hadamard_block:
+        import dataclasses
+        w = dataclasses.replace(w, hadamard_block=args.hadamard_block)
     total = args.warmup + args.steps + 12
 
     print("bench: building %d int4 caches for %s" % (args.caches, w.name), file=sys.stderr, flush=True)

@@ -290,6 +290,148 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a)
     }
 }
 
+// ---------------------------------------------------------------------------------------------
+// append of single positions (INT4_PROT): one wave per (task, kv head) for a task that writes one
+// position.  Lane l holds dims PL*(l % 32) .. +PL-1 of the K row (l < 32) or the V row (l >= 32):
+// the butterfly stages of span < PL run in the lane, the others pair lanes l and l ^ (span / PL)
+// of the same row (same stage order and arithmetic as the page-task kernel, so the results are
+// the same bits).  The V nibbles of the slot are merged into their bytes with a read-modify-write
+// whose loads are issued together with the row loads.
+// ---------------------------------------------------------------------------------------------
+
+template <int D>
+__global__ __launch_bounds__(64) void append_token_kernel(AppendArgs a)
+{
+    constexpr int PL = D / 32; // dims per lane
+    const AppendTask tk = a.tasks[blockIdx.x];
+    const int h = blockIdx.y;
+    const int lane = threadIdx.x;
+    const int row = lane >> 5; // 0: K, 1: V
+    const int l32 = lane & 31;
+    const int d0 = PL * l32;
+    const int slot = tk.t0 & (kPageSize - 1);
+    if (lane == 0 && h == 0 && (tk.flags & kTaskNewPage)) a.bt[tk.bt_index] = tk.page;
+    uint8_t* pb = a.pool + ((int64_t)tk.page * a.hkv + h) * a.page_block;
+
+    // row values and the V bytes that hold this slot's nibbles (loaded by all lanes, used by V)
+    const uint16_t* src = (row ? a.v : a.k) + ((int64_t)tk.row0 * a.hkv + h) * D + d0;
+    uint16_t raw[PL];
+#pragma unroll
+    for (int j = 0; j < PL; j++) raw[j] = src[j];
+    uint8_t* vbyte = pb + 8 * D + d0 * 8 + (slot >> 1);
+    uint8_t old[PL];
+#pragma unroll
+    for (int j = 0; j < PL; j++) old[j] = vbyte[8 * j];
+
+    float y[PL];
+#pragma unroll
+    for (int j = 0; j < PL; j++) y[j] = as_float((uint32_t)raw[j] << 16);
+    // stages h = 1, 2, ... < b in order
+#pragma unroll
+    for (int hh = 1; hh < PL; hh <<= 1) {
+        if (hh < a.block) {
+#pragma unroll
+            for (int i = 0; i < PL; i++) {
+                if ((i & hh) == 0) {
+                    const float a0 = y[i], c0 = y[i + hh];
+                    y[i] = a0 + c0;
+                    y[i + hh] = a0 - c0;
+                }
+            }
+        }
+    }
+    for (int hh = PL; hh < a.block; hh <<= 1) {
+        const int m = hh / PL;
+#pragma unroll
+        for (int i = 0; i < PL; i++) {
+            const float other = __shfl_xor(y[i], m, 64);
+            y[i] = (l32 & m) ? other - y[i] : y[i] + other;
+        }
+    }
+    if (a.block > 1) {
+#pragma unroll
+        for (int i = 0; i < PL; i++) y[i] = y[i] * a.cb;
+    }
+    // row min / max over the 32 lanes of the row
+    float mn = y[0], mx = y[0];
+#pragma unroll
+    for (int i = 1; i < PL; i++) {
+        mn = fminf(mn, y[i]);
+        mx = fmaxf(mx, y[i]);
+    }
+#pragma unroll
+    for (int m = 1; m < 32; m <<= 1) {
+        mn = fminf(mn, __shfl_xor(mn, m, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, m, 64));
+    }
+
+    // ---- INT4 page copy ----
+    {
+        const QuantParams qp = quant_params(mn, mx, 15.0f);
+        uint32_t c[PL];
+#pragma unroll
+        for (int i = 0; i < PL; i++) c[i] = __builtin_amdgcn_cvt_pk_u8_f32((y[i] - qp.zf) * qp.inv, 0, 0u);
+        if (row == 0) {
+            // K: [D/32 chunks][16 slots][16 B], byte k of a chunk = dims 2k (low), 2k+1 (high)
+            uint8_t* dst = pb + (d0 / 32) * 256 + slot * 16 + (d0 % 32) / 2;
+#pragma unroll
+            for (int i = 0; i < PL; i += 2) dst[i / 2] = (uint8_t)(c[i] | (c[i + 1] << 4));
+        } else {
+            // V: [D dims][8 B], nibble s = slot s
+#pragma unroll
+            for (int j = 0; j < PL; j++) {
+                const uint32_t b = (slot & 1) ? ((old[j] & 0x0Fu) | (c[j] << 4)) : ((old[j] & 0xF0u) | c[j]);
+                vbyte[8 * j] = (uint8_t)b;
+            }
+        }
+        if (l32 == 0) *(uint32_t*)(pb + 16 * D + slot * 8 + row * 4) = qp.s_bits | (qp.z_bits << 16);
+    }
+
+    // ---- INT8 copy when the position is protected ----
+    const int t = tk.t0;
+    if (is_protected(t, tk.len_new, a.sinks, a.recent)) {
+        const QuantParams qp = quant_params(mn, mx, 255.0f);
+        const int u = (t < a.sinks) ? t : a.sinks + t % a.recent;
+        uint8_t* tb = a.int8_pool + (((int64_t)tk.seq * a.hkv + h) * a.int8_tiles + (u >> 4)) * a.int8_tile;
+        const int s8 = u & 15;
+        uint32_t c[PL];
+#pragma unroll
+        for (int i = 0; i < PL; i++) c[i] = __builtin_amdgcn_cvt_pk_u8_f32((y[i] - qp.zf) * qp.inv, 0, 0u);
+        constexpr int BB = 16 * D + 128; // the tile's two blocks
+        if (row == 0) {
+            // K of dims half x = d0 / (D/2): [D/32 chunks][16 slots][16 B], one byte per dim
+            const int x = d0 / (D / 2), dx = d0 % (D / 2);
+            uint8_t* dst = tb + x * BB + (dx / 16) * 256 + s8 * 16 + dx % 16;
+#pragma unroll
+            for (int i = 0; i < PL; i++) dst[i] = (uint8_t)c[i];
+        } else {
+            // V of slot s8: block s8 / 8, [D dims][8 B], byte s8 % 8
+            uint8_t* dst = tb + (s8 >> 3) * BB + 8 * D + d0 * 8 + (s8 & 7);
+#pragma unroll
+            for (int j = 0; j < PL; j++) dst[8 * j] = (uint8_t)c[j];
+        }
+        if (l32 == 0) {
+#pragma unroll
+            for (int x = 0; x < 2; x++) *(uint32_t*)(tb + x * BB + 16 * D + s8 * 8 + row * 4) = qp.s_bits | (qp.z_bits << 16);
+        }
+    }
+}
+
+hipError_t launch_append_token(int d, int n_tasks, const AppendArgs& a, hipStream_t stream)
+{
+    if (n_tasks <= 0) return hipSuccess;
+    dim3 grid((unsigned)n_tasks, (unsigned)a.hkv), block(64);
+    if (d == 64) {
+        hipLaunchKernelGGL((append_token_kernel<64>), grid, block, 0, stream, a);
+        return hipGetLastError();
+    }
+    if (d == 128) {
+        hipLaunchKernelGGL((append_token_kernel<128>), grid, block, 0, stream, a);
+        return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_append(int d, int format, int n_tasks, const AppendArgs& a, hipStream_t stream)
 {
     if (n_tasks <= 0) return hipSuccess;

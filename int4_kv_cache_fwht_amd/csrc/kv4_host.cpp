@@ -403,7 +403,13 @@ kv4_status kv4_append(kv4_cache_t h, int32_t n_seqs, const int32_t* seq_ids, con
         if (e == hipSuccess) e = hipEventRecord(ev[0], strm);
         if (e != hipSuccess) return hip_fail(h, e, "profiling event");
     }
-    e = kv4::launch_append(h->st.cfg.d, h->st.cfg.format, (int)tasks.size(), a, strm);
+    // decode-time appends (one position per sequence) take the per-position kernel
+    bool single = h->st.cfg.format == kv4::FMT_INT4_PROT;
+    for (const auto& tk : tasks) single = single && tk.n == 1;
+    if (single)
+        e = kv4::launch_append_token(h->st.cfg.d, (int)tasks.size(), a, strm);
+    else
+        e = kv4::launch_append(h->st.cfg.d, h->st.cfg.format, (int)tasks.size(), a, strm);
     if (e != hipSuccess) return hip_fail(h, e, "append launch");
     if (h->prof.on) {
         e = hipEventRecord(ev[1], strm);

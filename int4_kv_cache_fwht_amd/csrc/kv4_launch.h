@@ -40,6 +40,8 @@ struct DecodeArgs {
 };
 
 hipError_t launch_append(int d, int format, int n_tasks, const AppendArgs& a, hipStream_t stream);
+// INT4_PROT append where every task writes exactly one position.
+hipError_t launch_append_token(int d, int n_tasks, const AppendArgs& a, hipStream_t stream);
 hipError_t launch_decode_split(int d, int g, int format, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_merge(int d, int g, int format, const DecodeArgs& a, hipStream_t stream);
 // Workgroups of the split kernel (4 waves each) that fit on one compute unit at once.
