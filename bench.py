@@ -74,10 +74,17 @@ def decode_bytes(fmt, lens, w):
 
 
 def kernel_source_hash():
+    """Hash of the sources that define the decode kernels: kv4_decode.hip, the device helpers and
+    plain structs it includes, and the DecodeArgs struct of kv4_launch.h."""
+    csrc = os.path.join(ROOT, "int4_kv_cache_fwht_amd", "csrc")
     h = hashlib.sha256()
-    for name in ("kv4_decode.hip", "kv4_common.cuh", "kv4_launch.h", "kv4_device_types.h"):
-        with open(os.path.join(ROOT, "int4_kv_cache_fwht_amd", "csrc", name), "rb") as f:
+    for name in ("kv4_decode.hip", "kv4_common.cuh", "kv4_device_types.h"):
+        with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
+    with open(os.path.join(csrc, "kv4_launch.h")) as f:
+        text = f.read()
+    i = text.index("struct DecodeArgs")
+    h.update(text[i:text.index("};", i)].encode())
     return h.hexdigest()[:16]
 
 
