@@ -303,7 +303,24 @@ template <int D>
 __global__ __launch_bounds__(64) void append_token_kernel(AppendArgs a)
 {
     constexpr int PL = D / 32; // dims per lane
-    const AppendTask tk = a.tasks[blockIdx.x];
+    AppendTask tk;
+    if (a.n_arg > 0) {
+        // task e from the argument block (read in place from the kernarg segment)
+        const int e = blockIdx.x;
+        const __attribute__((address_space(4))) char* ka =
+            (const __attribute__((address_space(4))) char*)__builtin_amdgcn_kernarg_segment_ptr();
+        const int32_t pg = ((const __attribute__((address_space(4))) int32_t*)(ka + offsetof(AppendArgs, arg_page)))[e];
+        tk.seq = ((const __attribute__((address_space(4))) int32_t*)(ka + offsetof(AppendArgs, arg_seq)))[e];
+        tk.t0 = ((const __attribute__((address_space(4))) int32_t*)(ka + offsetof(AppendArgs, arg_t0)))[e];
+        tk.page = pg & 0x7FFFFFFF;
+        tk.flags = pg < 0 ? kTaskNewPage : 0;
+        tk.n = 1;
+        tk.row0 = e;
+        tk.len_new = tk.t0 + 1;
+        tk.bt_index = tk.seq * a.max_pps + tk.t0 / kPageSize;
+    } else {
+        tk = a.tasks[blockIdx.x];
+    }
     const int h = blockIdx.y;
     const int lane = threadIdx.x;
     const int row = lane >> 5; // 0: K, 1: V

@@ -61,6 +61,94 @@ __device__ __forceinline__ DecodeUnit ld_unit(const DecodeUnit* units, int u)
     return r;
 }
 
+// A field of the kernel's own argument block, read in place from the kernarg segment.
+template <typename T>
+__device__ __forceinline__ const __attribute__((address_space(4))) T* kernarg_field(size_t offset)
+{
+    return (const __attribute__((address_space(4))) T*)((const __attribute__((address_space(4))) char*)
+                                                            __builtin_amdgcn_kernarg_segment_ptr() + offset);
+}
+
+// Steps of one (entry, kv head) unit at length L (the host planner's rule).
+template <int FMT>
+__device__ __forceinline__ int unit_steps_dev(const DecodeArgs& a, int L, int n8)
+{
+    if (FMT == FMT_INT4_PROT) {
+        const int lo = a.sinks, hi = L - a.recent;
+        const int pages = hi > lo ? (hi - 1) / kPageSize + 1 - lo / kPageSize : 0;
+        return n8 + (pages + kInt4StepPages - 1) / kInt4StepPages;
+    }
+    const int pages = (L + kPageSize - 1) / kPageSize;
+    if (FMT == FMT_INT8) return (pages + kInt8StepPages - 1) / kInt8StepPages;
+    return pages;
+}
+
+__device__ __forceinline__ int wave_incl_scan(int x, int lane)
+{
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+    }
+    return x;
+}
+
+// Argument plan: lane l holds, for entries l + 64 j, the first global step of the entry's units
+// (ex) and the steps of each of its units (st).
+struct EntryScan {
+    int32_t ex[4], st[4];
+};
+
+__device__ __forceinline__ int32_t pick4(const int32_t (&x)[4], int j)
+{
+    return j == 0 ? x[0] : j == 1 ? x[1] : j == 2 ? x[2] : x[3];
+}
+
+template <int FMT>
+__device__ EntryScan scan_entries(const DecodeArgs& a, int lane, int n8)
+{
+    const auto* lenp = kernarg_field<int32_t>(offsetof(DecodeArgs, arg_len));
+    EntryScan r;
+    int carry = 0;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const int e = 64 * j + lane;
+        const int st = (e < a.n_arg) ? unit_steps_dev<FMT>(a, lenp[e], n8) : 0;
+        const int tot = st * a.hkv;
+        const int incl = wave_incl_scan(tot, lane);
+        r.ex[j] = carry + incl - tot;
+        r.st[j] = st;
+        carry += __builtin_amdgcn_readlane(incl, 63);
+    }
+    return r;
+}
+
+// Unit u of the argument plan and the end of its step range.
+__device__ __forceinline__ void arg_unit(const DecodeArgs& a, const EntryScan& es, int u, DecodeUnit& U, int64_t& ue)
+{
+    const int e = u / a.hkv, h = u - e * a.hkv;
+    const int ex = __builtin_amdgcn_readlane(pick4(es.ex, e >> 6), e & 63);
+    const int st = __builtin_amdgcn_readlane(pick4(es.st, e >> 6), e & 63);
+    U.seq = kernarg_field<int32_t>(offsetof(DecodeArgs, arg_seq))[e];
+    U.len = kernarg_field<int32_t>(offsetof(DecodeArgs, arg_len))[e];
+    U.entry = e;
+    U.head = h;
+    U.step_begin = (int64_t)ex + (int64_t)h * st;
+    ue = U.step_begin + st;
+}
+
+// The unit of the argument plan that holds global step s.
+__device__ __forceinline__ int arg_first_unit(const DecodeArgs& a, const EntryScan& es, int lane, int64_t s)
+{
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < 4; j++) cnt += __builtin_popcountll(__ballot(64 * j + lane < a.n_arg && es.ex[j] <= s));
+    const int e = cnt - 1;
+    const int ex = __builtin_amdgcn_readlane(pick4(es.ex, e >> 6), e & 63);
+    const int st = __builtin_amdgcn_readlane(pick4(es.st, e >> 6), e & 63);
+    return e * a.hkv + (int)((s - ex) / st);
+}
+
 // s_waitcnt vmcnt(0), other counters untouched (gfx9 encoding)
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
@@ -104,6 +192,7 @@ struct DecodeWave {
     const int64_t s_end; // one past the wave's last global step
     const int n8;        // INT8 steps at the start of an INT4_PROT unit
 
+    EntryScan es; // argument plan (a.n_arg > 0)
     half4_t A4[NPAIR], A8[NPAIR];
     short4_t Abf[NPAIR_BF];
     float4_t acc[NHV][2]; // two accumulation chains per output half
@@ -584,12 +673,24 @@ struct DecodeWave {
         }
     }
 
+    // unit u and the end of its step range, from the argument plan or the uploaded one
+    __device__ __forceinline__ void unit_at(int u, DecodeUnit& U, int64_t& ue) const
+    {
+        if (a.n_arg > 0) {
+            arg_unit(a, es, u, U, ue);
+        } else {
+            U = ld_unit(a.units, u);
+            ue = (u + 1 < a.n_units) ? ld_uniform(&a.units[u + 1].step_begin) : a.total_steps;
+        }
+    }
+
     // ---- the wave's steps [s, s_end), starting in unit u (quantized formats) ----
     __device__ void run(int u, int64_t s)
     {
         while (s < s_end) {
-            const DecodeUnit U = ld_unit(a.units, u);
-            const int64_t ue = (u + 1 < a.n_units) ? ld_uniform(&a.units[u + 1].step_begin) : a.total_steps;
+            DecodeUnit U;
+            int64_t ue;
+            unit_at(u, U, ue);
             const int k0 = (int)(s - U.step_begin);
             const int k1 = (int)((s_end < ue ? s_end : ue) - U.step_begin);
             run_unit(U, k0, k1);
@@ -724,8 +825,9 @@ struct DecodeWave {
     __device__ void run_bf16(int u, int64_t s)
     {
         while (s < s_end) {
-            const DecodeUnit U = ld_unit(a.units, u);
-            const int64_t ue = (u + 1 < a.n_units) ? ld_uniform(&a.units[u + 1].step_begin) : a.total_steps;
+            DecodeUnit U;
+            int64_t ue;
+            unit_at(u, U, ue);
             const int k0 = (int)(s - U.step_begin);
             const int k1 = (int)((s_end < ue ? s_end : ue) - U.step_begin);
             prologue_bf16(U);
@@ -750,15 +852,21 @@ void decode_split_kernel(DecodeArgs a)
     const int64_t s = w * T / W;
     const int64_t s_end = (w + 1) * T / W;
     if (s >= s_end) return;
-    int lo = 0, hi = a.n_units - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (ld_uniform(&a.units[mid].step_begin) <= s)
-            lo = mid;
-        else
-            hi = mid - 1;
-    }
     DecodeWave<D, G, FMT> dw(a, lane, lds_all[wv], lds_all[wv] + kLdsQBytes, w, s_end);
+    int lo = 0;
+    if (a.n_arg > 0) {
+        dw.es = scan_entries<FMT>(a, lane, dw.n8);
+        lo = arg_first_unit(a, dw.es, lane, s);
+    } else {
+        int hi = a.n_units - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (ld_uniform(&a.units[mid].step_begin) <= s)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+    }
     if constexpr (FMT == FMT_BF16)
         dw.run_bf16(lo, s);
     else
@@ -777,17 +885,28 @@ __device__ __forceinline__ int64_t wave_of_step(int64_t step, int64_t T, int64_t
     return w < W - 1 ? w : W - 1;
 }
 
-template <int D, int G, bool ROT>
+template <int D, int G, int FMT>
 __global__ __launch_bounds__(64 * G) void merge_kernel(DecodeArgs a)
 {
     constexpr int NHV = D / 64;
+    constexpr bool ROT = FMT != FMT_BF16;
     const int u = blockIdx.x;
     const int i = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const DecodeUnit U = ld_unit(a.units, u);
+    DecodeUnit U;
+    int64_t se;
+    if (a.n_arg > 0) {
+        const int n8 = (FMT == FMT_INT4_PROT && a.sinks + a.recent > 0)
+                           ? (a.sinks + a.recent + kInt8StepSlots - 1) / kInt8StepSlots
+                           : 0;
+        const EntryScan es = scan_entries<FMT>(a, lane, n8);
+        arg_unit(a, es, u, U, se);
+    } else {
+        U = ld_unit(a.units, u);
+        se = (u + 1 < a.n_units) ? ld_uniform(&a.units[u + 1].step_begin) : a.total_steps;
+    }
     const int64_t T = a.total_steps, W = a.n_waves;
     const int64_t sb = U.step_begin;
-    const int64_t se = (u + 1 < a.n_units) ? ld_uniform(&a.units[u + 1].step_begin) : T;
     const int64_t w0 = wave_of_step(sb, T, W), w1 = wave_of_step(se - 1, T, W);
     const int n = (int)(w1 - w0 + 1);
     // partial j of this unit sits at index w0 + u + j; (m, l) are read with scalar loads (the split
@@ -850,7 +969,7 @@ static hipError_t launch_split_t(const DecodeArgs& a, hipStream_t stream)
 template <int D, int G, int F>
 static hipError_t launch_merge_t(const DecodeArgs& a, hipStream_t stream)
 {
-    hipLaunchKernelGGL((merge_kernel<D, G, F != FMT_BF16>), dim3((unsigned)a.n_units), dim3(64 * G), 0, stream, a);
+    hipLaunchKernelGGL((merge_kernel<D, G, F>), dim3((unsigned)a.n_units), dim3(64 * G), 0, stream, a);
     return hipGetLastError();
 }
 

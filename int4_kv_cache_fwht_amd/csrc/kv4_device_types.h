@@ -10,6 +10,7 @@ constexpr int kInt4StepPages = 4;   // decode INT4 step: 4 pages = 64 positions,
 constexpr int kInt8StepSlots = 32;  // decode INT8 step over protection slots: 2 tiles = 32 slots
 constexpr int kInt8StepPages = 2;   // decode step of the INT8 format: 2 pages = 32 positions
 constexpr int kWavesPerBlock = 4;   // decode split kernel: independent waves per workgroup
+constexpr int kArgEntries = 256;    // calls with up to this many sequences pass their plan as kernel arguments
 
 enum { kTaskNewPage = 1 };
 

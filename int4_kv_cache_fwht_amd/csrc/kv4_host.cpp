@@ -371,19 +371,37 @@ kv4_status kv4_append(kv4_cache_t h, int32_t n_seqs, const int32_t* seq_ids, con
     DeviceGuard g(h->device);
     if (g.err != hipSuccess) return hip_fail(h, g.err, "hipSetDevice");
     hipStream_t strm = (hipStream_t)stream;
-    const size_t bytes = tasks.size() * sizeof(kv4::AppendTask);
-    void* host = nullptr;
-    int slot = 0;
-    hipError_t e = h->staging.acquire(bytes, &host, &slot);
-    if (e != hipSuccess) return hip_fail(h, e, "staging");
-    std::memcpy(host, tasks.data(), bytes);
-    e = hipMemcpyAsync(workspace, host, bytes, hipMemcpyHostToDevice, strm);
-    if (e != hipSuccess) return hip_fail(h, e, "hipMemcpyAsync");
-    e = h->staging.commit(slot, strm);
-    if (e != hipSuccess) return hip_fail(h, e, "hipEventRecord");
+    // decode-time appends (one position per sequence) take the per-position kernel; up to
+    // kArgEntries of them travel in the kernel arguments instead of an uploaded task list
+    bool single = h->st.cfg.format == kv4::FMT_INT4_PROT;
+    for (const auto& tk : tasks) single = single && tk.n == 1;
+    const bool argplan = single && tasks.size() <= (size_t)kv4::kArgEntries;
+    hipError_t e = hipSuccess;
+    if (!argplan) {
+        const size_t bytes = tasks.size() * sizeof(kv4::AppendTask);
+        void* host = nullptr;
+        int slot = 0;
+        e = h->staging.acquire(bytes, &host, &slot);
+        if (e != hipSuccess) return hip_fail(h, e, "staging");
+        std::memcpy(host, tasks.data(), bytes);
+        e = hipMemcpyAsync(workspace, host, bytes, hipMemcpyHostToDevice, strm);
+        if (e != hipSuccess) return hip_fail(h, e, "hipMemcpyAsync");
+        e = h->staging.commit(slot, strm);
+        if (e != hipSuccess) return hip_fail(h, e, "hipEventRecord");
+    }
 
     kv4::AppendArgs a;
     a.tasks = (const kv4::AppendTask*)workspace;
+    a.max_pps = h->st.cfg.max_pps;
+    a.n_arg = 0;
+    if (argplan) {
+        a.n_arg = (int)tasks.size();
+        for (size_t i = 0; i < tasks.size(); i++) {
+            a.arg_seq[i] = tasks[i].seq;
+            a.arg_t0[i] = tasks[i].t0;
+            a.arg_page[i] = (int32_t)((uint32_t)tasks[i].page | ((tasks[i].flags & kv4::kTaskNewPage) ? 0x80000000u : 0u));
+        }
+    }
     a.k = (const uint16_t*)k_new;
     a.v = (const uint16_t*)v_new;
     a.pool = (uint8_t*)h->bufs.page_pool;
@@ -403,9 +421,6 @@ kv4_status kv4_append(kv4_cache_t h, int32_t n_seqs, const int32_t* seq_ids, con
         if (e == hipSuccess) e = hipEventRecord(ev[0], strm);
         if (e != hipSuccess) return hip_fail(h, e, "profiling event");
     }
-    // decode-time appends (one position per sequence) take the per-position kernel
-    bool single = h->st.cfg.format == kv4::FMT_INT4_PROT;
-    for (const auto& tk : tasks) single = single && tk.n == 1;
     if (single)
         e = kv4::launch_append_token(h->st.cfg.d, (int)tasks.size(), a, strm);
     else
@@ -459,15 +474,20 @@ kv4_status kv4_decode_attention(kv4_cache_t h, int32_t n_seqs, const int32_t* se
     if (g.err != hipSuccess) return hip_fail(h, g.err, "hipSetDevice");
     hipStream_t strm = (hipStream_t)stream;
     const size_t ubytes = (size_t)n_units * sizeof(kv4::DecodeUnit);
-    void* host = nullptr;
-    int slot = 0;
-    hipError_t e = h->staging.acquire(ubytes, &host, &slot);
-    if (e != hipSuccess) return hip_fail(h, e, "staging");
-    std::memcpy(host, units.data(), ubytes);
-    e = hipMemcpyAsync(workspace, host, ubytes, hipMemcpyHostToDevice, strm);
-    if (e != hipSuccess) return hip_fail(h, e, "hipMemcpyAsync");
-    e = h->staging.commit(slot, strm);
-    if (e != hipSuccess) return hip_fail(h, e, "hipEventRecord");
+    // up to kArgEntries sequences: the plan is the entry list in the kernel arguments (no upload)
+    const bool argplan = n_seqs <= kv4::kArgEntries && total < ((int64_t)1 << 31);
+    hipError_t e = hipSuccess;
+    if (!argplan) {
+        void* host = nullptr;
+        int slot = 0;
+        e = h->staging.acquire(ubytes, &host, &slot);
+        if (e != hipSuccess) return hip_fail(h, e, "staging");
+        std::memcpy(host, units.data(), ubytes);
+        e = hipMemcpyAsync(workspace, host, ubytes, hipMemcpyHostToDevice, strm);
+        if (e != hipSuccess) return hip_fail(h, e, "hipMemcpyAsync");
+        e = h->staging.commit(slot, strm);
+        if (e != hipSuccess) return hip_fail(h, e, "hipEventRecord");
+    }
 
     const int G = h->st.cfg.hq / h->st.cfg.hkv;
     const int D = h->st.cfg.d;
@@ -496,6 +516,14 @@ kv4_status kv4_decode_attention(kv4_cache_t h, int32_t n_seqs, const int32_t* se
     a.cb = h->cb;
     const double sc = scale > 0.f ? (double)scale : 1.0 / std::sqrt((double)D);
     a.scale_log2 = (float)(sc * 1.4426950408889634);
+    a.n_arg = 0;
+    if (argplan) {
+        a.n_arg = n_seqs;
+        for (int i = 0; i < n_seqs; i++) {
+            a.arg_seq[i] = seq_ids[i];
+            a.arg_len[i] = h->st.len[(size_t)seq_ids[i]];
+        }
+    }
     std::vector<hipEvent_t> ev;
     if (h->prof.on) {
         e = Profiler::make(3, &ev);

@@ -19,6 +19,14 @@ struct AppendArgs {
     int64_t int8_tile;
     int hkv, block, sinks, recent, int8_tiles;
     float cb; // fl32(1/sqrt(block))
+    int max_pps;
+    // single-position appends of up to kArgEntries sequences: task e writes position arg_t0[e] of
+    // sequence arg_seq[e] from row e into page arg_page[e] & 0x7fffffff (bit 31: allocated by
+    // this call).  n_arg == 0: the tasks come from `tasks`.
+    int n_arg;
+    int32_t arg_seq[kArgEntries];
+    int32_t arg_t0[kArgEntries];
+    int32_t arg_page[kArgEntries];
 };
 
 struct DecodeArgs {
@@ -37,6 +45,11 @@ struct DecodeArgs {
     int hkv, max_pps, sinks, recent, block, int8_tiles;
     float cb;         // fl32(1/sqrt(block))
     float scale_log2; // softmax scale * log2(e)
+    // n_arg > 0: the plan is this list of call entries (sequence id, length); unit u is entry
+    // u / hkv, kv head u % hkv, and the step ranges follow from the lengths.  n_arg == 0: `units`.
+    int n_arg;
+    int32_t arg_seq[kArgEntries];
+    int32_t arg_len[kArgEntries];
 };
 
 hipError_t launch_append(int d, int format, int n_tasks, const AppendArgs& a, hipStream_t stream);

@@ -210,3 +210,28 @@ def test_host_errors_leave_state_unchanged():
     assert (c.free_pages(), c.block_table(0), c.seq_length(0)) == before
     c.append([1, 2], [32, 16], k[:48].contiguous(), v[:48].contiguous())    # 2 + 1 pages: fits exactly
     assert c.free_pages() == 0
+
+
+def test_uploaded_plan_path():
+    """More sequences than the kernel arguments carry (300 > 256): the decode plan and the
+    single-position append tasks are uploaded instead.  Ragged lengths, two decode steps."""
+    _print_case("uploaded plan", n=300)
+    hq, hkv, d = 8, 2, 64
+    n = 300
+    rng = np.random.default_rng(9)
+    lens = [int(x) for x in rng.integers(1, 200, n)]
+    p = Pair(hq, hkv, d, num_pages=sum(math.ceil((L + 2) / 16) for L in lens) + n, max_seqs=n, max_pps=16,
+             S=4, R=32, b=64)
+    ch = W.outlier_channels(hkv, d, 2, 9)
+    ks, vs = zip(*[W.seq_kv(hkv, d, L, ch, 10.0, 9, 0, i, "cuda") for i, L in enumerate(lens)])
+    p.append(list(range(n)), lens, torch.cat(ks).contiguous(), torch.cat(vs).contiguous())
+    ids = [int(x) for x in rng.permutation(n)]
+    for step in range(2):
+        kn, vn = W.seq_kv(hkv, d, n, ch, 10.0, 9, 50 + step, 0, "cuda")
+        p.append(ids, [1] * n, kn, vn)
+        q = W.queries(n, hq, d, 9, step=step, device="cuda")
+        out, ref = p.decode(ids, q)
+        err = np.abs(out - ref).max()
+        print("uploaded plan step", step, "max-abs", err, flush=True)
+        assert err <= TOL
+    assert p.compare_cache([ids[0], ids[1], 17, 299]) > 0
