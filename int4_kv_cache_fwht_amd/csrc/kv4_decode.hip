@@ -83,70 +83,85 @@ __device__ __forceinline__ int unit_steps_dev(const DecodeArgs& a, int L, int n8
     return pages;
 }
 
-__device__ __forceinline__ int wave_incl_scan(int x, int lane)
-{
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
-    }
-    return x;
-}
-
-// Argument plan: lane l holds, for entries l + 64 j, the first global step of the entry's units
-// (ex) and the steps of each of its units (st).
-struct EntryScan {
-    int32_t ex[4], st[4];
+// Argument plan held in registers: lane l holds entries l + 64 j (first global step, sequence id,
+// length), loaded in one batch of vector loads; a wave looks entries up with readlane.
+struct EntryRegs {
+    int32_t step[kArgEntries / 64], seq[kArgEntries / 64], len[kArgEntries / 64];
 };
 
-__device__ __forceinline__ int32_t pick4(const int32_t (&x)[4], int j)
+// Lane l of register j of x (j, l wave-uniform): every register is read at lane l first and the
+// scalar results are selected, so the register array is never indexed at run time.
+template <int N>
+__device__ __forceinline__ int32_t lane_pick(const int32_t (&x)[N], int j, int l)
 {
-    return j == 0 ? x[0] : j == 1 ? x[1] : j == 2 ? x[2] : x[3];
-}
-
-template <int FMT>
-__device__ EntryScan scan_entries(const DecodeArgs& a, int lane, int n8)
-{
-    const auto* lenp = kernarg_field<int32_t>(offsetof(DecodeArgs, arg_len));
-    EntryScan r;
-    int carry = 0;
+    int32_t r = __builtin_amdgcn_readlane(x[0], l);
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-        const int e = 64 * j + lane;
-        const int st = (e < a.n_arg) ? unit_steps_dev<FMT>(a, lenp[e], n8) : 0;
-        const int tot = st * a.hkv;
-        const int incl = wave_incl_scan(tot, lane);
-        r.ex[j] = carry + incl - tot;
-        r.st[j] = st;
-        carry += __builtin_amdgcn_readlane(incl, 63);
+    for (int i = 1; i < N; i++) {
+        const int32_t v = __builtin_amdgcn_readlane(x[i], l);
+        r = (j == i) ? v : r;
     }
     return r;
 }
 
-// Unit u of the argument plan and the end of its step range.
-__device__ __forceinline__ void arg_unit(const DecodeArgs& a, const EntryScan& es, int u, DecodeUnit& U, int64_t& ue)
+__device__ __forceinline__ EntryRegs load_entries(const DecodeArgs& a, int lane)
+{
+    const auto* stp = kernarg_field<int32_t>(offsetof(DecodeArgs, arg_step));
+    const auto* seqp = kernarg_field<int32_t>(offsetof(DecodeArgs, arg_seq));
+    const auto* lenp = kernarg_field<int32_t>(offsetof(DecodeArgs, arg_len));
+    EntryRegs r;
+#pragma unroll
+    for (int j = 0; j < kArgEntries / 64; j++) {
+        const int e = 64 * j + lane;
+        const int ec = e < a.n_arg ? e : 0;
+        r.step[j] = e < a.n_arg ? stp[ec] : 0x7FFFFFFF;
+        r.seq[j] = seqp[ec];
+        r.len[j] = lenp[ec];
+    }
+    return r;
+}
+
+// Unit u of the argument plan (entries in registers) and the end of its step range.
+template <int FMT>
+__device__ __forceinline__ void arg_unit(const DecodeArgs& a, const EntryRegs& er, int n8, int u, DecodeUnit& U,
+                                         int64_t& ue)
 {
     const int e = u / a.hkv, h = u - e * a.hkv;
-    const int ex = __builtin_amdgcn_readlane(pick4(es.ex, e >> 6), e & 63);
-    const int st = __builtin_amdgcn_readlane(pick4(es.st, e >> 6), e & 63);
-    U.seq = kernarg_field<int32_t>(offsetof(DecodeArgs, arg_seq))[e];
-    U.len = kernarg_field<int32_t>(offsetof(DecodeArgs, arg_len))[e];
+    const int j = e >> 6, l = e & 63;
+    U.seq = lane_pick(er.seq, j, l);
+    U.len = lane_pick(er.len, j, l);
     U.entry = e;
     U.head = h;
-    U.step_begin = (int64_t)ex + (int64_t)h * st;
+    const int st = unit_steps_dev<FMT>(a, U.len, n8);
+    U.step_begin = (int64_t)lane_pick(er.step, j, l) + (int64_t)h * st;
     ue = U.step_begin + st;
 }
 
 // The unit of the argument plan that holds global step s.
-__device__ __forceinline__ int arg_first_unit(const DecodeArgs& a, const EntryScan& es, int lane, int64_t s)
+template <int FMT>
+__device__ __forceinline__ int arg_first_unit(const DecodeArgs& a, const EntryRegs& er, int n8, int64_t s)
 {
     int cnt = 0;
 #pragma unroll
-    for (int j = 0; j < 4; j++) cnt += __builtin_popcountll(__ballot(64 * j + lane < a.n_arg && es.ex[j] <= s));
+    for (int j = 0; j < kArgEntries / 64; j++) cnt += __builtin_popcountll(__ballot(er.step[j] <= s));
     const int e = cnt - 1;
-    const int ex = __builtin_amdgcn_readlane(pick4(es.ex, e >> 6), e & 63);
-    const int st = __builtin_amdgcn_readlane(pick4(es.st, e >> 6), e & 63);
-    return e * a.hkv + (int)((s - ex) / st);
+    const int j = e >> 6, l = e & 63;
+    const int len = lane_pick(er.len, j, l);
+    const int ex = lane_pick(er.step, j, l);
+    return e * a.hkv + (int)((s - ex) / unit_steps_dev<FMT>(a, len, n8));
+}
+
+// Unit u of the argument plan read with scalar loads (the merge kernel's single lookup).
+template <int FMT>
+__device__ __forceinline__ void arg_unit_scalar(const DecodeArgs& a, int n8, int u, DecodeUnit& U, int64_t& ue)
+{
+    const int e = u / a.hkv, h = u - e * a.hkv;
+    U.seq = kernarg_field<int32_t>(offsetof(DecodeArgs, arg_seq))[e];
+    U.len = kernarg_field<int32_t>(offsetof(DecodeArgs, arg_len))[e];
+    U.entry = e;
+    U.head = h;
+    const int st = unit_steps_dev<FMT>(a, U.len, n8);
+    U.step_begin = (int64_t)kernarg_field<int32_t>(offsetof(DecodeArgs, arg_step))[e] + (int64_t)h * st;
+    ue = U.step_begin + st;
 }
 
 // s_waitcnt vmcnt(0), other counters untouched (gfx9 encoding)
@@ -192,7 +207,7 @@ struct DecodeWave {
     const int64_t s_end; // one past the wave's last global step
     const int n8;        // INT8 steps at the start of an INT4_PROT unit
 
-    EntryScan es; // argument plan (a.n_arg > 0)
+    EntryRegs er; // argument plan (a.n_arg > 0)
     half4_t A4[NPAIR], A8[NPAIR];
     short4_t Abf[NPAIR_BF];
     float4_t acc[NHV][2]; // two accumulation chains per output half
@@ -677,7 +692,7 @@ struct DecodeWave {
     __device__ __forceinline__ void unit_at(int u, DecodeUnit& U, int64_t& ue) const
     {
         if (a.n_arg > 0) {
-            arg_unit(a, es, u, U, ue);
+            arg_unit<FMT>(a, er, n8, u, U, ue);
         } else {
             U = ld_unit(a.units, u);
             ue = (u + 1 < a.n_units) ? ld_uniform(&a.units[u + 1].step_begin) : a.total_steps;
@@ -855,8 +870,8 @@ void decode_split_kernel(DecodeArgs a)
     DecodeWave<D, G, FMT> dw(a, lane, lds_all[wv], lds_all[wv] + kLdsQBytes, w, s_end);
     int lo = 0;
     if (a.n_arg > 0) {
-        dw.es = scan_entries<FMT>(a, lane, dw.n8);
-        lo = arg_first_unit(a, dw.es, lane, s);
+        dw.er = load_entries(a, lane);
+        lo = arg_first_unit<FMT>(a, dw.er, dw.n8, s);
     } else {
         int hi = a.n_units - 1;
         while (lo < hi) {
@@ -899,8 +914,7 @@ __global__ __launch_bounds__(64 * G) void merge_kernel(DecodeArgs a)
         const int n8 = (FMT == FMT_INT4_PROT && a.sinks + a.recent > 0)
                            ? (a.sinks + a.recent + kInt8StepSlots - 1) / kInt8StepSlots
                            : 0;
-        const EntryScan es = scan_entries<FMT>(a, lane, n8);
-        arg_unit(a, es, u, U, se);
+        arg_unit_scalar<FMT>(a, n8, u, U, se);
     } else {
         U = ld_unit(a.units, u);
         se = (u + 1 < a.n_units) ? ld_uniform(&a.units[u + 1].step_begin) : a.total_steps;

@@ -522,6 +522,7 @@ kv4_status kv4_decode_attention(kv4_cache_t h, int32_t n_seqs, const int32_t* se
         for (int i = 0; i < n_seqs; i++) {
             a.arg_seq[i] = seq_ids[i];
             a.arg_len[i] = h->st.len[(size_t)seq_ids[i]];
+            a.arg_step[i] = (int32_t)units[(size_t)i * h->st.cfg.hkv].step_begin;
         }
     }
     std::vector<hipEvent_t> ev;

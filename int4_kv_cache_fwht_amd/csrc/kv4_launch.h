@@ -45,11 +45,13 @@ struct DecodeArgs {
     int hkv, max_pps, sinks, recent, block, int8_tiles;
     float cb;         // fl32(1/sqrt(block))
     float scale_log2; // softmax scale * log2(e)
-    // n_arg > 0: the plan is this list of call entries (sequence id, length); unit u is entry
-    // u / hkv, kv head u % hkv, and the step ranges follow from the lengths.  n_arg == 0: `units`.
+    // n_arg > 0: the plan is this list of call entries: sequence id, length and the first global
+    // step of the entry's units; unit u is entry u / hkv, kv head u % hkv, and its steps follow
+    // from the length.  n_arg == 0: `units`.
     int n_arg;
     int32_t arg_seq[kArgEntries];
     int32_t arg_len[kArgEntries];
+    int32_t arg_step[kArgEntries];
 };
 
 hipError_t launch_append(int d, int format, int n_tasks, const AppendArgs& a, hipStream_t stream);
