@@ -40,9 +40,12 @@ def parse():
     ap.add_argument("--baseline-steps", type=int, default=12)
     ap.add_argument("--cpu-baseline-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-quality", action="store_true", help="skip the decode-error diagnostic")
     ap.add_argument("--decode-waves", type=int, default=0)
     ap.add_argument("--hadamard-block", type=int, default=0,
                     help="override the workload's Hadamard block (1 = plain INT4: no q / output rotation)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU run: write the measured decode traffic from two rocprofv3 --pmc output folders")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference kernel for PMC byte counters)")
     return ap.parse_args()
@@ -232,6 +235,60 @@ def cpu_baseline(w, seconds, device):
                 n_s, sum(lens[:n_s]), w.name, reps, el)}
 
 
+QUALITY_VARIANTS = [
+    # name, format, hadamard block (0 = workload's), sinks, recent (None = workload's)
+    ("int4_rot_prot", "int4", 0, None, None),
+    ("int4_rot_noprot", "int4", 0, 0, 0),
+    ("int4_norot_prot", "int4", 1, None, None),
+    ("int4_rot_sinks_only", "int4", 0, None, 0),
+    ("int4_rot_recent_only", "int4", 0, 0, None),
+    ("int4_plain", "int4", 1, 0, 0),
+    ("int8", "int8", 0, 0, 0),
+    ("bf16", "bf16", 1, 0, 0),
+]
+
+
+def quality(w, device, n_seqs=4):
+    """Diagnostic: decode error of each storage variant against exact attention (fp64, numpy) on the
+    unquantized bf16 K / V of a seeded sample of the workload's sequences."""
+    import numpy as np
+    import torch
+    import int4_kv_cache_fwht_amd as kv4
+    import kv4_inputs as W
+    lens = w.lengths()[:n_seqs]
+    ch = W.outlier_channels(w.num_kv_heads, w.head_dim, w.outlier_channels, w.seed)
+    kvs = [W.seq_kv(w.num_kv_heads, w.head_dim, L, ch, w.outlier_scale, w.seed, 0, i, device) for i, L in enumerate(lens)]
+    q = W.queries(len(lens), w.num_q_heads, w.head_dim, w.seed, device=device)
+    G = w.num_q_heads // w.num_kv_heads
+    scale = 1.0 / math.sqrt(w.head_dim)
+    qf = q.float().cpu().numpy().astype(np.float64)
+    ref = np.zeros(qf.shape)
+    for i, (k, v) in enumerate(kvs):
+        kf = k.float().cpu().numpy().astype(np.float64)
+        vf = v.float().cpu().numpy().astype(np.float64)
+        for g in range(w.num_q_heads):
+            e = kf[:, g // G, :] @ qf[i, g] * scale
+            p_ = np.exp(e - e.max())
+            ref[i, g] = (p_ / p_.sum()) @ vf[:, g // G, :]
+    res = {}
+    for name, fmt, block, S, R in QUALITY_VARIANTS:
+        cfg = kv4.Config(num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+                         num_pages=sum(math.ceil(L / 16) for L in lens) + 4, max_seqs=len(lens),
+                         max_pages_per_seq=max(math.ceil(L / 16) for L in lens) + 1,
+                         num_sinks=w.num_sinks if S is None else S, num_recent=w.num_recent if R is None else R,
+                         hadamard_block=block or w.hadamard_block, format=FORMATS[fmt])
+        cache = kv4.Cache(cfg, device)
+        cache.append(list(range(len(lens))), lens, torch.cat([k for k, _ in kvs]).contiguous(),
+                     torch.cat([v for _, v in kvs]).contiguous())
+        out = cache.decode_attention(list(range(len(lens))), q).cpu().numpy().astype(np.float64)
+        err = out - ref
+        res[name] = {"max_abs": float(np.abs(err).max()),
+                     "rel_rms": float(np.sqrt((err ** 2).mean() / (ref ** 2).mean()))}
+        del cache
+    return {"reference": "exact fp64 attention on the unquantized bf16 K/V, %d sequences (%d positions)" % (
+        len(lens), sum(lens)), "errors": res}
+
+
 def copy_probe(device):
     """Plain device copy of 1 GiB (the reference kernel for PMC byte counters) -> GB/s moved."""
     import torch
@@ -302,8 +359,63 @@ def append_workload(device, repeats=7):
             "note": "best of %d repeats; kernel time from HIP events on the call's stream" % repeats}
 
 
+def write_traffic(fetch_dir, write_dir, workload, fmt="int4"):
+    """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE; both with
+    --copy-calibration) into the measured HBM bytes per decode-split launch, each counter scaled by
+    what it reads for the plain 1 GiB copy; stores them, keyed by the decode sources' hash, in
+    profiles/decode_split_traffic.json."""
+    import csv
+    import glob
+
+    def per_kernel(root, counter):
+        vals = {}
+        for f in glob.glob(os.path.join(root, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                for row in csv.DictReader(fh):
+                    if row["Counter_Name"] == counter:
+                        vals.setdefault(row.get("Kernel_Name", ""), []).append(float(row["Counter_Value"]))
+        return vals
+
+    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    kname = "kv4::decode_split_kernel<128, 4, %d>" % FORMATS[fmt]
+    pick = lambda vals: next(v for k, v in vals.items() if kname in k)
+    copy_f = max(v for k, vs in fetch.items() if "copyBuffer" in k for v in vs)
+    copy_w = max(v for k, vs in write.items() if "copyBuffer" in k for v in vs)
+    n = 1 << 30
+    ff, wf = n / (copy_f * 1024), n / (copy_w * 1024)
+    f_kib, w_kib = pick(fetch), pick(write)
+    fb = sum(f_kib) / len(f_kib) * 1024 * ff
+    wb = sum(w_kib) / len(w_kib) * 1024 * wf
+    path = os.path.join(ROOT, "profiles", "decode_split_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        rec = {}
+    cmd = ("rocprofv3 --pmc %s --kernel-include-regex 'kv4|copyBuffer|copy' --output-format csv -d %s -o run -- "
+           "python bench.py --workload %s --steps 4 --warmup 1 --baselines '' --no-cpu-baseline --no-quality "
+           "--copy-calibration")
+    rec["%s/%s" % (workload, fmt)] = {
+        "kernel": "decode_split_kernel<128,4,%s>" % {"int4": "INT4_PROT", "int8": "INT8", "bf16": "BF16"}[fmt],
+        "kernel_source_hash": kernel_source_hash(),
+        "bytes_per_launch": fb + wb, "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
+        "fetch_size_kib_mean": sum(f_kib) / len(f_kib), "write_size_kib_mean": sum(w_kib) / len(w_kib),
+        "dispatches": len(f_kib),
+        "copy_reference": {"bytes_read": n, "bytes_written": n, "fetch_size_kib": copy_f, "write_size_kib": copy_w,
+                           "fetch_factor": ff, "write_factor": wf},
+        "commands": [cmd % ("FETCH_SIZE", fetch_dir, workload), cmd % ("WRITE_SIZE", write_dir, workload),
+                     "python bench.py --workload %s --traffic-from %s %s" % (workload, fetch_dir, write_dir)],
+    }
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    return rec["%s/%s" % (workload, fmt)]
+
+
 def main():
     args = parse()
+    if args.traffic_from:
+        print(json.dumps(write_traffic(args.traffic_from[0], args.traffic_from[1], args.workload)))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on exactly one GPU: the decode path is built and measured on one GPU "
               "(multi-GPU sharding is not built); use --gpus 1", file=sys.stderr)
@@ -375,6 +487,9 @@ def main():
         result["baselines"] = base
     if args.copy_calibration:
         result["copy_probe_GBps"] = copy_probe(device)
+    if not args.no_quality:
+        print("bench: quality diagnostic", file=sys.stderr, flush=True)
+        result["quality"] = quality(w, device)
     if not args.no_cpu_baseline:
         print("bench: cpu baseline", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_baseline_seconds, device)
