@@ -104,6 +104,8 @@ def lib():
         L.kv4o_dequant_seq.restype = c_int
         L.kv4o_decode.argtypes = [P, c_int, P, P, c_double, P, c_int, P]
         L.kv4o_decode.restype = c_int
+        L.kv4o_attend_multi.argtypes = [P, c_int, P, P, P, c_double, P, c_int, P]
+        L.kv4o_attend_multi.restype = c_int
         _lib = L
     return _lib
 
@@ -320,4 +322,23 @@ class OracleCache:
                                ctypes.byref(used))
         if rc != OK:
             raise ValueError("oracle decode failed (%d)" % rc)
+        return out, used.value
+
+    def attend_multi(self, seq_ids: Sequence[int], n_q: Sequence[int], q_bits: np.ndarray, scale: float = 0.0,
+                     threads: int = 0) -> Tuple[np.ndarray, int]:
+        """Causal attention of the last n_q[i] positions of each sequence over its cache.
+        q_bits: uint16 [sum n_q, hq, d] bf16 patterns, rows of a sequence consecutive (ascending
+        position) -> (out float64 [sum n_q, hq, d], threads used)."""
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int32)
+        nq = np.ascontiguousarray(n_q, dtype=np.int32)
+        assert nq.shape == ids.shape
+        rows = int(nq.sum())
+        q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
+        assert q_bits.shape == (rows, self.hq, self.d)
+        out = np.zeros((rows, self.hq, self.d), dtype=np.float64)
+        used = ctypes.c_int()
+        rc = lib().kv4o_attend_multi(self._h, ids.shape[0], _ptr(ids), _ptr(nq), _ptr(q_bits), float(scale), _ptr(out),
+                                     int(threads), ctypes.byref(used))
+        if rc != OK:
+            raise ValueError("oracle multi-query attention failed (%d)" % rc)
         return out, used.value

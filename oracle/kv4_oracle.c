@@ -677,8 +677,12 @@ int kv4o_dequant_seq(const kv4o_cache* c, int seq, int h, double* k_out, double*
 }
 
 /* One (sequence, kv head) unit: the G query heads that share kv head h (query head g reads kv
- * head g / G).  q: [hq][d] bf16 bits of this sequence; out: [hq][d] binary64. */
-static int decode_unit(const kv4o_cache* c, int seq, int h, const uint16_t* q, double scale, double* out)
+ * head g / G), for nq query rows.  Query row r sits at position p = L - nq + r of the sequence
+ * (length L) and attends positions 0 .. p; every position is read from the copy that decode
+ * reads at length L (the INT8 slot when it is in Prot(L), else its page).  nq = 1 is decode
+ * attention over all L positions.  q: [nq][hq][d] bf16 bits of this sequence; out: [nq][hq][d]
+ * binary64. */
+static int attend_unit(const kv4o_cache* c, int seq, int h, int nq, const uint16_t* q, double scale, double* out)
 {
     int d = c->d, G = c->hq / c->hkv, L = c->len[seq];
     int rotated = (c->fmt != KV4O_FMT_BF16);
@@ -694,41 +698,46 @@ static int decode_unit(const kv4o_cache* c, int seq, int h, const uint16_t* q, d
         return KV4O_INVALID_ARGUMENT;
     }
     int rc = kv4o_dequant_seq(c, seq, h, kb, vb);
-    for (int gi = 0; gi < G && rc == KV4O_OK; gi++) {
-        int g = h * G + gi;
-        double* qd = qr;
-        double* qrot = qr + d;
-        double* o = qr + 2 * d;
-        for (int i = 0; i < d; i++)
-            qd[i] = (double)bf16_to_float(q[(size_t)g * d + i]);
-        if (rotated)
-            hadamard_f64(qd, d, c->b, qrot);
-        else
-            memcpy(qrot, qd, (size_t)d * sizeof(double));
-        double m = -INFINITY;
-        for (int t = 0; t < L; t++) {
-            double acc = 0.0;
+    for (int r = 0; r < nq && rc == KV4O_OK; r++) {
+        int n = L - nq + r + 1; /* positions attended by row r */
+        for (int gi = 0; gi < G; gi++) {
+            int g = h * G + gi;
+            const uint16_t* qrow = q + ((size_t)r * c->hq + g) * d;
+            double* orow = out + ((size_t)r * c->hq + g) * d;
+            double* qd = qr;
+            double* qrot = qr + d;
+            double* o = qr + 2 * d;
             for (int i = 0; i < d; i++)
-                acc += qrot[i] * kb[(size_t)t * d + i];
-            e[t] = scale * acc;
-            if (e[t] > m)
-                m = e[t];
+                qd[i] = (double)bf16_to_float(qrow[i]);
+            if (rotated)
+                hadamard_f64(qd, d, c->b, qrot);
+            else
+                memcpy(qrot, qd, (size_t)d * sizeof(double));
+            double m = -INFINITY;
+            for (int t = 0; t < n; t++) {
+                double acc = 0.0;
+                for (int i = 0; i < d; i++)
+                    acc += qrot[i] * kb[(size_t)t * d + i];
+                e[t] = scale * acc;
+                if (e[t] > m)
+                    m = e[t];
+            }
+            double l = 0.0;
+            for (int t = 0; t < n; t++) {
+                e[t] = exp(e[t] - m);
+                l += e[t];
+            }
+            for (int i = 0; i < d; i++) {
+                double acc = 0.0;
+                for (int t = 0; t < n; t++)
+                    acc += e[t] * vb[(size_t)t * d + i];
+                o[i] = acc / l;
+            }
+            if (rotated)
+                hadamard_f64(o, d, c->b, orow);
+            else
+                memcpy(orow, o, (size_t)d * sizeof(double));
         }
-        double l = 0.0;
-        for (int t = 0; t < L; t++) {
-            e[t] = exp(e[t] - m);
-            l += e[t];
-        }
-        for (int i = 0; i < d; i++) {
-            double acc = 0.0;
-            for (int t = 0; t < L; t++)
-                acc += e[t] * vb[(size_t)t * d + i];
-            o[i] = acc / l;
-        }
-        if (rotated)
-            hadamard_f64(o, d, c->b, out + (size_t)g * d);
-        else
-            memcpy(out + (size_t)g * d, o, (size_t)d * sizeof(double));
     }
     free(kb);
     free(vb);
@@ -741,6 +750,8 @@ typedef struct {
     const kv4o_cache* c;
     int n_seqs;
     const int* seq_ids;
+    const int* n_q;     /* query rows per sequence (NULL: one each) */
+    const size_t* row0; /* first query row of each sequence */
     const uint16_t* q;
     double scale;
     double* out;
@@ -761,8 +772,9 @@ static void* decode_worker(void* arg)
         if (w >= job->n_seqs * c->hkv)
             break;
         int i = w / c->hkv, h = w % c->hkv;
-        int rc = decode_unit(c, job->seq_ids[i], h, job->q + (size_t)i * per_seq, job->scale,
-                             job->out + (size_t)i * per_seq);
+        int nq = job->n_q ? job->n_q[i] : 1;
+        size_t r0 = job->row0 ? job->row0[i] : (size_t)i;
+        int rc = attend_unit(c, job->seq_ids[i], h, nq, job->q + r0 * per_seq, job->scale, job->out + r0 * per_seq);
         if (rc != KV4O_OK) {
             pthread_mutex_lock(&job->lock);
             job->rc = rc;
@@ -772,23 +784,32 @@ static void* decode_worker(void* arg)
     return NULL;
 }
 
-/* Decode attention for a batch: q [n_seqs][hq][d] bf16 bits, out [n_seqs][hq][d] binary64.
- * scale <= 0 selects 1/sqrt(d).  Every listed sequence must have length >= 1.  Work is spread
- * over n_threads threads (0: all online processors); *threads_used reports the count. */
-int kv4o_decode(const kv4o_cache* c, int n_seqs, const int* seq_ids, const uint16_t* q, double scale, double* out,
-                int n_threads, int* threads_used)
+static int run_attend(const kv4o_cache* c, int n_seqs, const int* seq_ids, const int* n_q, const uint16_t* q,
+                      double scale, double* out, int n_threads, int* threads_used)
 {
     if (n_seqs < 0)
         return KV4O_INVALID_ARGUMENT;
+    size_t* row0 = (size_t*)malloc(((size_t)n_seqs + 1) * sizeof(size_t));
+    if (!row0)
+        return KV4O_INVALID_ARGUMENT;
+    row0[0] = 0;
     for (int i = 0; i < n_seqs; i++) {
         int s = seq_ids[i];
-        if (s < 0 || s >= c->max_seqs)
+        int nq = n_q ? n_q[i] : 1;
+        if (s < 0 || s >= c->max_seqs || nq < 1) {
+            free(row0);
             return KV4O_INVALID_ARGUMENT;
+        }
         for (int j = 0; j < i; j++)
-            if (seq_ids[j] == s)
+            if (seq_ids[j] == s) {
+                free(row0);
                 return KV4O_INVALID_ARGUMENT;
-        if (c->len[s] < 1)
+            }
+        if (c->len[s] < nq) {
+            free(row0);
             return KV4O_SEQ_STATE;
+        }
+        row0[i + 1] = row0[i] + (size_t)nq;
     }
     if (scale <= 0)
         scale = 1.0 / sqrt((double)c->d);
@@ -802,6 +823,8 @@ int kv4o_decode(const kv4o_cache* c, int n_seqs, const int* seq_ids, const uint1
     job.c = c;
     job.n_seqs = n_seqs;
     job.seq_ids = seq_ids;
+    job.n_q = n_q;
+    job.row0 = row0;
     job.q = q;
     job.scale = scale;
     job.out = out;
@@ -817,8 +840,29 @@ int kv4o_decode(const kv4o_cache* c, int n_seqs, const int* seq_ids, const uint1
     for (int i = 0; i < started; i++)
         pthread_join(th[i], NULL);
     free(th);
+    free(row0);
     pthread_mutex_destroy(&job.lock);
     if (threads_used)
         *threads_used = started + 1;
     return job.rc;
+}
+
+/* Decode attention for a batch: q [n_seqs][hq][d] bf16 bits, out [n_seqs][hq][d] binary64.
+ * scale <= 0 selects 1/sqrt(d).  Every listed sequence must have length >= 1.  Work is spread
+ * over n_threads threads (0: all online processors); *threads_used reports the count. */
+int kv4o_decode(const kv4o_cache* c, int n_seqs, const int* seq_ids, const uint16_t* q, double scale, double* out,
+                int n_threads, int* threads_used)
+{
+    return run_attend(c, n_seqs, seq_ids, NULL, q, scale, out, n_threads, threads_used);
+}
+
+/* Causal attention of several query rows per sequence over the cache as it stands: the n_q[i]
+ * rows of sequence seq_ids[i] (length L, 1 <= n_q[i] <= L) sit at positions L - n_q[i] .. L - 1
+ * and row r attends positions 0 .. L - n_q[i] + r, each read from the copy decode reads at
+ * length L.  q: [sum n_q][hq][d] bf16 bits, rows of a sequence consecutive, sequences in call
+ * order; out: the same shape, binary64. */
+int kv4o_attend_multi(const kv4o_cache* c, int n_seqs, const int* seq_ids, const int* n_q, const uint16_t* q,
+                      double scale, double* out, int n_threads, int* threads_used)
+{
+    return run_attend(c, n_seqs, seq_ids, n_q, q, scale, out, n_threads, threads_used);
 }
