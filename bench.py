@@ -23,6 +23,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA
 METRIC = "INT4-KV decode attention kv-tokens/s and achieved HBM GB/s (% of MI355X peak)"
 FORMATS = {"int4": 0, "int8": 1, "bf16": 2}
 
@@ -33,8 +34,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=40)
     ap.add_argument("--warmup", type=int, default=4)
     ap.add_argument("--workload", default="qwen3_8b_layer",
-                    choices=["qwen3_8b_layer", "rollout", "long_context", "tiny", "append"],
-                    help="decode workloads, or 'append': the append path alone at Hadamard block 128 vs 1")
+                    choices=["qwen3_8b_layer", "rollout", "long_context", "tiny", "append", "multi_query"],
+                    help="decode workloads; 'append': the append path alone at Hadamard block 128 vs 1; "
+                         "'multi_query': causal multi-query attention on the Qwen3-8B-shaped layer")
+    ap.add_argument("--mq-rows", type=int, default=4, help="query rows per sequence of the multi_query workload")
     ap.add_argument("--caches", type=int, default=4, help="distinct layer caches cycled (defeats the 256 MB MALL)")
     ap.add_argument("--baselines", default="int8,bf16", help="comma list of baseline formats ('' for none)")
     ap.add_argument("--baseline-steps", type=int, default=12)
@@ -359,6 +362,100 @@ def append_workload(device, repeats=7):
             "note": "best of %d repeats; kernel time from HIP events on the call's stream" % repeats}
 
 
+def mq_workload(device, n_q, steps, warmup, n_caches=4):
+    """Multi-query attention on the Qwen3-8B-shaped layer (64 sequences, lengths uniform in
+    [1024, 8192]): each step appends n_q positions to every sequence of one of n_caches layer
+    caches (cycled, as in the decode bench) and then attends with the n_q new positions as causal
+    query rows.  Returns the JSON record."""
+    import torch
+    import int4_kv_cache_fwht_amd as kv4
+    import kv4_inputs as W
+    w = W.WORKLOADS["qwen3_8b_layer"]
+    hq, hkv, d, B = w.num_q_heads, w.num_kv_heads, w.head_dim, w.batch
+    lens0 = w.lengths()
+    prof_steps = 12
+    total = warmup + steps + prof_steps
+    growth = (total // n_caches + 1) * n_q
+    pages = sum(math.ceil((L + growth) / 16) for L in lens0) + B
+    ch = W.outlier_channels(hkv, d, w.outlier_channels, w.seed)
+    caches, lens = [], []
+    for c in range(n_caches):
+        cfg = kv4.Config(num_q_heads=hq, num_kv_heads=hkv, head_dim=d, num_pages=pages, max_seqs=B,
+                         max_pages_per_seq=math.ceil((max(lens0) + growth) / 16) + 1, num_sinks=w.num_sinks,
+                         num_recent=w.num_recent, hadamard_block=w.hadamard_block, format=0)
+        cache = kv4.Cache(cfg, device)
+        for i, L in enumerate(lens0):
+            k, v = W.seq_kv(hkv, d, L, ch, w.outlier_scale, w.seed, c, i, device)
+            cache.append([i], [L], k, v)
+        caches.append(cache)
+        lens.append(list(lens0))
+    ids = list(range(B))
+    kn, qs = [], []
+    for st in range(total):
+        kn.append(W.seq_kv(hkv, d, B * n_q, ch, w.outlier_scale, w.seed, 5000 + st, 0, device))
+        qs.append(W.queries(B * n_q, hq, d, w.seed, step=st, device=device))
+    out = torch.empty((B * n_q, hq, d), dtype=torch.float32, device=device)
+    state = {"i": 0}
+
+    def one():
+        st = state["i"]
+        c = st % n_caches
+        caches[c].append(ids, [n_q] * B, kn[st][0], kn[st][1])
+        caches[c].multi_query_attention(ids, [n_q] * B, qs[st], out=out)
+        lens[c] = [L + n_q for L in lens[c]]
+        state["i"] += 1
+        return lens[c]
+
+    for _ in range(warmup):
+        one()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    attended = 0
+    for _ in range(steps):
+        ls = one()
+        attended += sum(n_q * L - n_q * (n_q - 1) // 2 for L in ls)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    for c in caches:
+        c.profile_enable(True)
+    nbytes = flops = 0
+    for _ in range(prof_steps):
+        ls = one()
+        nbytes += decode_bytes("int4", ls, w) + len(ls) * (n_q - 1) * hq * d * 6
+        flops += sum(n_q * L - n_q * (n_q - 1) // 2 for L in ls) * hq * 4 * d
+    tot = {"mq_split_ms": 0.0, "mq_merge_ms": 0.0, "append_ms": 0.0, "mq_launches": 0, "append_launches": 0}
+    for c in caches:
+        p = c.profile_read()
+        for k in tot:
+            tot[k] += p[k]
+        c.profile_enable(False)
+    split_s = tot["mq_split_ms"] / tot["mq_launches"] * 1e-3
+    bytes_launch, flops_launch = nbytes / prof_steps, flops / prof_steps
+    gbps = bytes_launch / split_s / 1e9
+    tflops = flops_launch / split_s / 1e12
+    intensity = flops_launch / bytes_launch
+    ridge = MFMA_F16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    if intensity < ridge:
+        roof = {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS}
+    else:
+        roof = {"bound": "mfma", "achieved": tflops, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": tflops / MFMA_F16_PEAK_TFLOPS}
+    roof.update({"traffic": None, "kernel": "mq_split_kernel<128,4,INT4_PROT>", "avg_launch_us": split_s * 1e6,
+                 "algorithmic_bytes_per_launch": bytes_launch, "algorithmic_flops_per_launch": flops_launch,
+                 "achieved_GBps": gbps, "achieved_TFLOPs": tflops, "flops_per_byte": intensity})
+    return {"metric": "INT4-KV multi-query attention: attended (query row, position) pairs per s", "value":
+            attended / el, "unit": "row-positions/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+            "ms_per_step": el / steps * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "f32", "data": "synthetic",
+            "config": {"workload": "multi_query", "batch": B, "query_rows_per_seq": n_q, "kv_heads": hkv,
+                       "q_heads": hq, "head_dim": d, "context": "uniform[1024, 8192] + growth", "sinks": w.num_sinks,
+                       "recent": w.num_recent, "hadamard_block": w.hadamard_block, "distinct_caches": n_caches},
+            "roofline": roof,
+            "step_breakdown_us": {"append": tot["append_ms"] / max(tot["append_launches"], 1) * 1e3,
+                                  "mq_split": split_s * 1e6,
+                                  "mq_merge": tot["mq_merge_ms"] / tot["mq_launches"] * 1e3}}
+
+
 def write_traffic(fetch_dir, write_dir, workload, fmt="int4"):
     """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE; both with
     --copy-calibration) into the measured HBM bytes per decode-split launch, each counter scaled by
@@ -426,6 +523,9 @@ def main():
     device = torch.device("cuda", 0)
     if args.workload == "append":
         print(json.dumps(append_workload(device)), flush=True)
+        return
+    if args.workload == "multi_query":
+        print(json.dumps(mq_workload(device, args.mq_rows, args.steps, args.warmup)), flush=True)
         return
     w = W.WORKLOADS[args.workload]
     if args.hadamard_block:

@@ -174,6 +174,31 @@ kv4_status kv4_decode_attention(kv4_cache_t h, int32_t n_seqs, const int32_t* se
                                 float scale, float* out, void* workspace, size_t ws_bytes,
                                 void* stream /* hipStream_t */);
 
+/* Device workspace needed by kv4_multi_query_attention for exactly this argument list and the
+ * cache's current lengths (query it for the call it is meant for).  Errors as for the call. */
+kv4_status kv4_multi_query_workspace_size(kv4_cache_t h, int32_t n_seqs, const int32_t* seq_ids,
+                                          const int32_t* n_q, size_t* bytes);
+
+/*
+ * Causal attention of several query positions per sequence over the cache as it stands (a
+ * prefill chunk attending the cache after the chunk's own append, or the tokens of a multi-token
+ * decode step).  The pages define no such call; it extends the fused attention of [SAW] with the
+ * reading stated here.  For each i (ids distinct, length L >= n_q[i] >= 1), the n_q[i] query rows
+ * of sequence seq_ids[i] sit at positions L - n_q[i] .. L - 1, and row r attends positions
+ * 0 .. L - n_q[i] + r, each read from the copy decode reads at length L (the INT8 slot when the
+ * position is in Prot(L), else its INT4 page copy):
+ *   out[row][g] = sum_{t <= pos(row)} softmax_t(scale * <q_g H, k^_t>) v^_t H^T
+ * n_q[i] = 1 for every i is decode attention.
+ *   q   (device) bf16 [sum n_q][Hq][D]: the rows of a sequence consecutive in ascending position,
+ *       sequences in call order;
+ *   out (device) fp32, the same shape and order.
+ * Formats: INT4_PROT and INT8 (BF16: UNSUPPORTED).  scale <= 0 selects 1/sqrt(D).
+ * Errors: INVALID_ARGUMENT, SEQ_STATE (length 0 or n_q > L), UNSUPPORTED, WORKSPACE_TOO_SMALL, HIP.
+ */
+kv4_status kv4_multi_query_attention(kv4_cache_t h, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_q,
+                                     const void* q, float scale, float* out, void* workspace, size_t ws_bytes,
+                                     void* stream /* hipStream_t */);
+
 /* Host-state queries. */
 kv4_status kv4_seq_length(kv4_cache_t h, int32_t seq_id, int32_t* len);
 kv4_status kv4_block_table(kv4_cache_t h, int32_t seq_id, int32_t* pages /* host */, int32_t cap, int32_t* n);
@@ -191,6 +216,9 @@ typedef struct kv4_profile {
     int64_t decode_launches;
     double split_ms;   /* decode split-KV kernels */
     double merge_ms;   /* decode merge + inverse-rotation kernels */
+    int64_t mq_launches;
+    double mq_split_ms;  /* multi-query split kernels */
+    double mq_merge_ms;  /* multi-query merge + inverse-rotation kernels */
 } kv4_profile;
 kv4_status kv4_profile_enable(kv4_cache_t h, int32_t enable);
 kv4_status kv4_profile_read(kv4_cache_t h, kv4_profile* out);

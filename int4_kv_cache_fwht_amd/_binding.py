@@ -47,7 +47,8 @@ class _BufferSizes(ctypes.Structure):
 
 class _Profile(ctypes.Structure):
     _fields_ = [("append_launches", ctypes.c_int64), ("append_ms", ctypes.c_double),
-                ("decode_launches", ctypes.c_int64), ("split_ms", ctypes.c_double), ("merge_ms", ctypes.c_double)]
+                ("decode_launches", ctypes.c_int64), ("split_ms", ctypes.c_double), ("merge_ms", ctypes.c_double),
+                ("mq_launches", ctypes.c_int64), ("mq_split_ms", ctypes.c_double), ("mq_merge_ms", ctypes.c_double)]
 
 
 class _Buffers(ctypes.Structure):
@@ -109,6 +110,8 @@ def lib():
         L.kv4_seq_free.argtypes = [P, I32]
         L.kv4_decode_workspace_size.argtypes = [P, I32, P]
         L.kv4_decode_attention.argtypes = [P, I32, P, P, ctypes.c_float, P, P, SZ, P]
+        L.kv4_multi_query_workspace_size.argtypes = [P, I32, P, P, P]
+        L.kv4_multi_query_attention.argtypes = [P, I32, P, P, P, ctypes.c_float, P, P, SZ, P]
         L.kv4_seq_length.argtypes = [P, I32, P]
         L.kv4_block_table.argtypes = [P, I32, P, I32, P]
         L.kv4_free_pages.argtypes = [P, P]
@@ -121,6 +124,7 @@ def lib():
         L.kv4_last_error.restype = ctypes.c_char_p
         for name in ("kv4_buffer_sizes_query", "kv4_cache_create", "kv4_cache_destroy", "kv4_append_workspace_size",
                      "kv4_append", "kv4_seq_free", "kv4_decode_workspace_size", "kv4_decode_attention",
+                     "kv4_multi_query_workspace_size", "kv4_multi_query_attention",
                      "kv4_seq_length", "kv4_block_table", "kv4_free_pages", "kv4_set_decode_waves",
                      "kv4_profile_enable", "kv4_profile_read"):
             getattr(L, name).restype = ctypes.c_int
@@ -181,6 +185,7 @@ class Cache:
         self._h = h
         self._ws_append = None
         self._ws_decode = None
+        self._ws_mq = None
 
     # -- lifetime --------------------------------------------------------------------------------
     def close(self):
@@ -257,6 +262,32 @@ class Cache:
                                           workspace.data_ptr(), workspace.numel(), st), self._h)
         return out
 
+    def multi_query_workspace_size(self, seq_ids: Sequence[int], n_q: Sequence[int]) -> int:
+        ids, nq = _i32_array(seq_ids), _i32_array(n_q)
+        out = ctypes.c_size_t()
+        _check(lib().kv4_multi_query_workspace_size(self._h, len(ids), ids, nq, ctypes.byref(out)), self._h)
+        return out.value
+
+    def multi_query_attention(self, seq_ids: Sequence[int], n_q: Sequence[int], q: torch.Tensor, scale: float = 0.0,
+                              out: Optional[torch.Tensor] = None, stream=None,
+                              workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """q: bf16 [sum(n_q), Hq, D] (each sequence's rows in ascending position) -> fp32, same shape."""
+        ids, nq = _i32_array(seq_ids), _i32_array(n_q)
+        rows = sum(int(x) for x in n_q)
+        shape = (rows, self.cfg.num_q_heads, self.cfg.head_dim)
+        if q.dtype != torch.bfloat16 or not q.is_contiguous() or tuple(q.shape) != shape or q.device != self.device:
+            raise ValueError("q must be a contiguous bf16 [sum(n_q), Hq, D] tensor on the cache device")
+        if out is None:
+            out = torch.empty(shape, dtype=torch.float32, device=self.device)
+        elif out.dtype != torch.float32 or not out.is_contiguous() or tuple(out.shape) != shape:
+            raise ValueError("out must be a contiguous fp32 [sum(n_q), Hq, D] tensor")
+        if workspace is None:
+            workspace = self._workspace("_ws_mq", self.multi_query_workspace_size(seq_ids, n_q))
+        st = _stream_ptr(stream)
+        _check(lib().kv4_multi_query_attention(self._h, len(ids), ids, nq, q.data_ptr(), float(scale), out.data_ptr(),
+                                               workspace.data_ptr(), workspace.numel(), st), self._h)
+        return out
+
     def seq_free(self, seq_id: int):
         _check(lib().kv4_seq_free(self._h, int(seq_id)), self._h)
 
@@ -287,4 +318,5 @@ class Cache:
         p = _Profile()
         _check(lib().kv4_profile_read(self._h, ctypes.byref(p)), self._h)
         return {"append_launches": p.append_launches, "append_ms": p.append_ms,
-                "decode_launches": p.decode_launches, "split_ms": p.split_ms, "merge_ms": p.merge_ms}
+                "decode_launches": p.decode_launches, "split_ms": p.split_ms, "merge_ms": p.merge_ms,
+                "mq_launches": p.mq_launches, "mq_split_ms": p.mq_split_ms, "mq_merge_ms": p.mq_merge_ms}

@@ -14,7 +14,7 @@ LIB = os.path.join(PKG, "libkv4.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
 ARCH = "gfx950"
-KERNEL_SOURCES = ["kv4_append.hip", "kv4_decode.hip"]
+KERNEL_SOURCES = ["kv4_append.hip", "kv4_decode.hip", "kv4_mq.hip"]
 # -ffp-contract=off: the append's binary32 steps must not fuse into FMAs.
 # -packed-fp32-ops off: no packed fp32 VALU instructions in any kernel.
 HIPFLAGS = [

@@ -84,6 +84,7 @@ struct Profiler {
     bool on = false;
     std::vector<std::vector<hipEvent_t>> append_ev; // {before, after}
     std::vector<std::vector<hipEvent_t>> decode_ev; // {before split, after split, after merge}
+    std::vector<std::vector<hipEvent_t>> mq_ev;     // the same for multi-query calls
     kv4_profile totals{};
 
     static hipError_t make(int n, std::vector<hipEvent_t>* out)
@@ -103,8 +104,12 @@ struct Profiler {
         for (auto& v : decode_ev)
             for (auto e : v)
                 if (e) hipEventDestroy(e);
+        for (auto& v : mq_ev)
+            for (auto e : v)
+                if (e) hipEventDestroy(e);
         append_ev.clear();
         decode_ev.clear();
+        mq_ev.clear();
         totals = kv4_profile{};
     }
     hipError_t collect()
@@ -131,6 +136,18 @@ struct Profiler {
             for (auto e : v) hipEventDestroy(e);
         }
         decode_ev.clear();
+        for (auto& v : mq_ev) {
+            hipError_t r = hipEventSynchronize(v[2]);
+            if (r != hipSuccess) return r;
+            float a = 0.f, b = 0.f;
+            hipEventElapsedTime(&a, v[0], v[1]);
+            hipEventElapsedTime(&b, v[1], v[2]);
+            totals.mq_launches += 1;
+            totals.mq_split_ms += a;
+            totals.mq_merge_ms += b;
+            for (auto e : v) hipEventDestroy(e);
+        }
+        mq_ev.clear();
         return hipSuccess;
     }
 };
@@ -147,6 +164,7 @@ struct kv4_cache {
     int device = 0;
     int num_cus = 256;
     int resident_waves = 2048; // decode split waves resident at once on the device
+    int mq_resident_waves = 2048; // multi-query split waves resident at once
     int decode_waves = 0; // 0: automatic
     float cb = 1.0f;
     Staging staging;
@@ -234,6 +252,17 @@ size_t decode_ws_bytes(const kv4_cache* h, int64_t n_units, int64_t waves)
            align_up((size_t)parts * G * D * sizeof(float));
 }
 
+// Multi-query split tasks: about two rounds of resident waves per call.
+int64_t mq_target_tasks(const kv4_cache* h) { return 2 * (int64_t)h->mq_resident_waves; }
+
+size_t mq_ws_bytes(const kv4_cache* h, const kv4::MqPlan& p)
+{
+    const int D = h->st.cfg.d;
+    return align_up(p.entries.size() * sizeof(kv4::MqEntry)) +
+           align_up((size_t)p.tasks * kv4::kMqRows * 2 * sizeof(float)) +
+           align_up((size_t)p.tasks * kv4::kMqRows * D * sizeof(float));
+}
+
 size_t append_task_bound(int32_t n_seqs, const int32_t* n_new)
 {
     size_t tasks = 0;
@@ -313,6 +342,15 @@ kv4_status kv4_cache_create(const kv4_config* cfg, const kv4_buffers* bufs, kv4_
             return hip_fail(nullptr, e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
         }
         h->resident_waves = (bpc > 0 ? bpc : 1) * kv4::kWavesPerBlock * h->num_cus;
+        bpc = 0;
+        if (c.format != kv4::FMT_BF16) {
+            e = kv4::mq_split_residency(c.d, c.hq / c.hkv, c.format, &bpc);
+            if (e != hipSuccess) {
+                delete h;
+                return hip_fail(nullptr, e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+            }
+        }
+        h->mq_resident_waves = (bpc > 0 ? bpc : 1) * 4 * h->num_cus;
     }
     h->cb = (float)(1.0 / std::sqrt((double)c.block));
     e = h->staging.init(8);
@@ -543,6 +581,99 @@ kv4_status kv4_decode_attention(kv4_cache_t h, int32_t n_seqs, const int32_t* se
         e = hipEventRecord(ev[2], strm);
         if (e != hipSuccess) return hip_fail(h, e, "profiling event");
         h->prof.decode_ev.push_back(ev);
+    }
+    return KV4_OK;
+}
+
+kv4_status kv4_multi_query_workspace_size(kv4_cache_t h, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_q,
+                                          size_t* bytes)
+{
+    if (!h || !bytes) return fail(h, KV4_ERR_INVALID_ARGUMENT, "null argument");
+    kv4::MqPlan plan;
+    std::string msg;
+    kv4::Status s = h->st.plan_multi(n_seqs, seq_ids, n_q, mq_target_tasks(h), &plan, &msg);
+    if (s != kv4::OK) return fail(h, (kv4_status)s, msg);
+    *bytes = mq_ws_bytes(h, plan);
+    return KV4_OK;
+}
+
+kv4_status kv4_multi_query_attention(kv4_cache_t h, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_q,
+                                     const void* q, float scale, float* out, void* workspace, size_t ws_bytes,
+                                     void* stream)
+{
+    if (!h) return fail(nullptr, KV4_ERR_INVALID_ARGUMENT, "null handle");
+    if (n_seqs < 0 || (n_seqs > 0 && (!seq_ids || !n_q || !q || !out)))
+        return fail(h, KV4_ERR_INVALID_ARGUMENT, "bad argument list");
+    if (!std::isfinite(scale)) return fail(h, KV4_ERR_INVALID_ARGUMENT, "scale must be finite");
+    kv4::MqPlan plan;
+    std::string msg;
+    kv4::Status s = h->st.plan_multi(n_seqs, seq_ids, n_q, mq_target_tasks(h), &plan, &msg);
+    if (s != kv4::OK) return fail(h, (kv4_status)s, msg);
+    if (plan.entries.empty()) return KV4_OK;
+    if (!workspace || ws_bytes < mq_ws_bytes(h, plan))
+        return fail(h, KV4_ERR_WORKSPACE_TOO_SMALL, "multi-query workspace too small");
+
+    DeviceGuard g(h->device);
+    if (g.err != hipSuccess) return hip_fail(h, g.err, "hipSetDevice");
+    hipStream_t strm = (hipStream_t)stream;
+    const size_t ebytes = plan.entries.size() * sizeof(kv4::MqEntry);
+    void* host = nullptr;
+    int slot = 0;
+    hipError_t e = h->staging.acquire(ebytes, &host, &slot);
+    if (e != hipSuccess) return hip_fail(h, e, "staging");
+    std::memcpy(host, plan.entries.data(), ebytes);
+    e = hipMemcpyAsync(workspace, host, ebytes, hipMemcpyHostToDevice, strm);
+    if (e != hipSuccess) return hip_fail(h, e, "hipMemcpyAsync");
+    e = h->staging.commit(slot, strm);
+    if (e != hipSuccess) return hip_fail(h, e, "hipEventRecord");
+
+    const int G = h->st.cfg.hq / h->st.cfg.hkv;
+    const int D = h->st.cfg.d;
+    uint8_t* ws = (uint8_t*)workspace;
+    kv4::MqArgs a;
+    a.pool = (const uint8_t*)h->bufs.page_pool;
+    a.int8_pool = (const uint8_t*)h->bufs.int8_pool;
+    a.bt = h->bufs.block_table;
+    a.q = (const uint16_t*)q;
+    a.entries = (const kv4::MqEntry*)ws;
+    a.part_ml = (float*)(ws + align_up(ebytes));
+    a.part_o = (float*)(ws + align_up(ebytes) + align_up((size_t)plan.tasks * kv4::kMqRows * 2 * sizeof(float)));
+    a.out = out;
+    a.page_block = (int64_t)h->sizes.page_block;
+    a.int8_tile = (int64_t)h->sizes.int8_tile;
+    a.n_entries = (int)plan.entries.size();
+    a.tasks = (int)plan.tasks;
+    a.groups = (int)plan.groups;
+    a.spc = plan.spc;
+    a.hq = h->st.cfg.hq;
+    a.hkv = h->st.cfg.hkv;
+    a.max_pps = h->st.cfg.max_pps;
+    a.sinks = h->st.cfg.sinks;
+    a.recent = h->st.cfg.recent;
+    a.block = h->st.cfg.block;
+    a.int8_tiles = h->sizes.int8_tiles;
+    a.n8 = kv4::mq_int8_steps(h->st.cfg);
+    a.cb = h->cb;
+    const double sc = scale > 0.f ? (double)scale : 1.0 / std::sqrt((double)D);
+    a.scale_log2 = (float)(sc * 1.4426950408889634);
+    std::vector<hipEvent_t> ev;
+    if (h->prof.on) {
+        e = Profiler::make(3, &ev);
+        if (e == hipSuccess) e = hipEventRecord(ev[0], strm);
+        if (e != hipSuccess) return hip_fail(h, e, "profiling event");
+    }
+    e = kv4::launch_mq_split(D, G, h->st.cfg.format, a, strm);
+    if (e != hipSuccess) return hip_fail(h, e, "multi-query split launch");
+    if (h->prof.on) {
+        e = hipEventRecord(ev[1], strm);
+        if (e != hipSuccess) return hip_fail(h, e, "profiling event");
+    }
+    e = kv4::launch_mq_merge(D, G, a, strm);
+    if (e != hipSuccess) return hip_fail(h, e, "multi-query merge launch");
+    if (h->prof.on) {
+        e = hipEventRecord(ev[2], strm);
+        if (e != hipSuccess) return hip_fail(h, e, "profiling event");
+        h->prof.mq_ev.push_back(ev);
     }
     return KV4_OK;
 }

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "kv4_device_types.h"
+#include "kv4_mq_types.h"
 
 namespace kv4 {
 
@@ -54,6 +55,23 @@ struct DecodeArgs {
     int32_t arg_step[kArgEntries];
 };
 
+struct MqArgs {
+    const uint8_t* pool;
+    const uint8_t* int8_pool;
+    const int32_t* bt;
+    const uint16_t* q;        // bf16 [rows][hq][D]
+    const MqEntry* entries;   // device copy of the plan
+    float* part_ml;           // [tasks][16][2]: (reference, sum of p) per query row, log2 units
+    float* part_o;            // [tasks][16][D]: unnormalised rotated output per query row
+    float* out;               // fp32 [rows][hq][D]
+    int64_t page_block;
+    int64_t int8_tile;
+    int n_entries, tasks, groups, spc;
+    int hq, hkv, max_pps, sinks, recent, block, int8_tiles, n8;
+    float cb;         // fl32(1/sqrt(block))
+    float scale_log2; // softmax scale * log2(e)
+};
+
 hipError_t launch_append(int d, int format, int n_tasks, const AppendArgs& a, hipStream_t stream);
 // INT4_PROT append where every task writes exactly one position.
 hipError_t launch_append_token(int d, int n_tasks, const AppendArgs& a, hipStream_t stream);
@@ -61,5 +79,10 @@ hipError_t launch_decode_split(int d, int g, int format, const DecodeArgs& a, hi
 hipError_t launch_decode_merge(int d, int g, int format, const DecodeArgs& a, hipStream_t stream);
 // Workgroups of the split kernel (4 waves each) that fit on one compute unit at once.
 hipError_t decode_split_residency(int d, int g, int format, int* blocks_per_cu);
+// Multi-query attention (INT4_PROT and INT8 formats): split kernel over the call's wave tasks,
+// then the merge that also applies the inverse rotation.
+hipError_t launch_mq_split(int d, int g, int format, const MqArgs& a, hipStream_t stream);
+hipError_t launch_mq_merge(int d, int g, const MqArgs& a, hipStream_t stream);
+hipError_t mq_split_residency(int d, int g, int format, int* blocks_per_cu);
 
 } // namespace kv4

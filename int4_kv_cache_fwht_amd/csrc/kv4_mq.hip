@@ -1,0 +1,627 @@
+// kv4_mq.hip -- causal multi-query attention over the paged INT4 cache with INT8 sink/recent
+// slots: several query positions per sequence (its last n positions: a prefill chunk, or the
+// tokens of a multi-token decode step), each attending the positions up to its own.
+// Sources: "SAW-INT4: System-Aware 4-Bit KV-Cache Quantization for Real-World LLM Serving",
+// Abstract (fused attention over a paged INT4 cache after a block-diagonal Hadamard rotation);
+// "KV4-RL: Unlocking Faster Asynchronous Rollouts for RLVR with INT4 KV Cache Quantization",
+// Abstract (sinks and recent context read from INT8).
+//
+// A wave takes 16 query rows -- (query position, query head) pairs that share one kv head -- and
+// a chunk of that (sequence, kv head)'s steps.  A step is 32 positions: two INT8 tiles (the
+// protection slots, first) or two INT4 pages.  Both products run on v_mfma_f32_16x16x32_f16:
+//   S^T = K Q^T:  the A operand is 16 positions' key codes as fp16 subnormal patterns (value
+//                 code * 2^-24, exact); the B operand the rotated query rows, scaled by a power of
+//                 two and split into hi + lo fp16.  A score is s_K (q . code) + z_K sum(q).
+//   O += P' V:    the A operand is p * s_V (hi + lo fp16), the B operand the value codes, which
+//                 the page stores dim-major, again as subnormal patterns; sum_t p_t z_V,t is
+//                 accumulated per lane.
+// Positions are assigned to the S^T rows so that the accumulator of lane l holds the scores of
+// query row l % 16 for 8 consecutive positions of the step -- exactly the positions whose p * s_V
+// lane l supplies to the PV operand, and whose value codes are one 4-byte (INT4) or 8-byte (INT8)
+// run of each dim row.  The two products therefore need no exchange between lanes.
+//
+// Softmax reference: per query row, the running maximum of score + (exponent field of s_V); it is
+// raised only when a step exceeds it by more than kMqTau (then the accumulators are rescaled).
+// This bounds p * s_V * 2^27 below 2^14, inside the fp16 range, whatever the value scales.
+#include "kv4_common.cuh"
+
+namespace kv4 {
+namespace {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+
+constexpr float kMqTau = 1.f;
+constexpr float kPScale = 134217728.f; // 2^27
+
+template <typename T>
+__device__ __forceinline__ T mq_uniform(const T* p)
+{
+    return *(const __attribute__((address_space(4))) T*)p;
+}
+
+__device__ __forceinline__ float4_t mfma16x32(u32x4 a, u32x4 b, float4_t c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b), c,
+                                                  0, 0, 0);
+}
+
+// Eight INT4 codes, nibble i = element i, as fp16 subnormal patterns in the element order
+// (0, 4, 1, 5, 2, 6, 3, 7).
+__device__ __forceinline__ u32x4 spread_int4(uint32_t w)
+{
+    return (u32x4){w & 0x000F000Fu, (w >> 4) & 0x000F000Fu, (w >> 8) & 0x000F000Fu, (w >> 12) & 0x000F000Fu};
+}
+
+// Eight INT8 codes (bytes of w0 = elements 0..3, of w1 = elements 4..7), same order.
+__device__ __forceinline__ u32x4 spread_int8(uint32_t w0, uint32_t w1)
+{
+    return (u32x4){__builtin_amdgcn_perm(w1, w0, 0x0C040C00u), __builtin_amdgcn_perm(w1, w0, 0x0C050C01u),
+                   __builtin_amdgcn_perm(w1, w0, 0x0C060C02u), __builtin_amdgcn_perm(w1, w0, 0x0C070C03u)};
+}
+
+// hi + lo fp16 of eight floats, same element order as the spreads.
+__device__ __forceinline__ void split_hilo(const float (&x)[8], u32x4& hi, u32x4& lo)
+{
+#pragma unroll
+    for (int s = 0; s < 4; s++) {
+        const _Float16 h0 = (_Float16)x[s], h1 = (_Float16)x[s + 4];
+        const _Float16 l0 = (_Float16)(x[s] - (float)h0), l1 = (_Float16)(x[s + 4] - (float)h1);
+        hi[s] = (uint32_t)f16_bits(h0) | ((uint32_t)f16_bits(h1) << 16);
+        lo[s] = (uint32_t)f16_bits(l0) | ((uint32_t)f16_bits(l1) << 16);
+    }
+}
+
+__device__ __forceinline__ u32x4 ld16(const uint8_t* p) { return *(const u32x4*)p; }
+__device__ __forceinline__ u32x2 ld8(const uint8_t* p) { return *(const u32x2*)p; }
+__device__ __forceinline__ uint32_t ld4(const uint8_t* p) { return *(const uint32_t*)p; }
+
+template <typename T>
+__device__ __forceinline__ const T* pick(bool c, const T* x, const T* y)
+{
+    return c ? x : y;
+}
+
+template <int D, int G, int FMT>
+struct MqWave {
+    static constexpr int KS = D / 32;   // k-steps of S^T = INT4 key-code dwords per tile and lane
+    static constexpr int NCB = D / 16;  // 16-dim column blocks of the output
+    static constexpr int DPL = D / 4;   // query dims per lane in the prologue
+    static constexpr int QT = kMqRows / G;
+    static constexpr int IB = 16 * D + 128; // bytes of an INT4 page block / an INT8 tile block
+
+    // One step's operands for this lane.  INT8 buffers hold twice the key and value bytes.
+    template <bool IS8>
+    struct Buf {
+        uint32_t k[2][IS8 ? 2 * KS : KS];
+        uint32_t v[NCB][IS8 ? 2 : 1];
+        uint32_t sc[16];
+    };
+
+    const MqArgs& a;
+    const int lane, n, g;
+    int seq, L, head, pos_r;
+    int lo4, hi4;        // INT4_PROT: INT4-read positions [S, L - R)
+    int ring_base, ring_mod; // INT4_PROT: first recent position and its residue mod R
+    const uint8_t* t8;   // INT4_PROT: this (sequence, kv head)'s INT8 tiles
+    const int32_t* btrow;
+    int p0, p1;          // INT4 page range (INT4_PROT) or page count (INT8 format: p1)
+    float m_ref = -__builtin_inff(), lsum = 0.f, zsum = 0.f, Ar = 0.f, Br = 0.f;
+    u32x4 qhi[KS], qlo[KS];
+    float4_t acc[NCB];
+
+    __device__ MqWave(const MqArgs& args, int l) : a(args), lane(l), n(l & 15), g(l >> 4) {}
+
+    // Rotated, scaled query row n: dims DPL*g .. DPL*g + DPL - 1 held by this lane.
+    __device__ void prologue(const MqEntry& e, int rt)
+    {
+        const int jq = rt * QT + n / G, gi = n % G;
+        const bool row_ok = jq < e.nq;
+        pos_r = row_ok ? e.len - e.nq + jq : -1;
+        const uint16_t* qp = a.q + ((int64_t)(e.qrow0 + (row_ok ? jq : 0)) * a.hq + head * G + gi) * D + DPL * g;
+        float x[DPL];
+#pragma unroll
+        for (int c = 0; c < DPL / 8; c++) {
+            const u32x4 u = ld16((const uint8_t*)(qp + 8 * c));
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                x[8 * c + 2 * j] = row_ok ? as_float(u[j] << 16) : 0.f;
+                x[8 * c + 2 * j + 1] = row_ok ? as_float(u[j] & 0xFFFF0000u) : 0.f;
+            }
+        }
+        // FWHT over blocks of `block` dims: in-lane stages, then across the lanes of the row
+#pragma unroll
+        for (int h = 1; h < DPL; h <<= 1) {
+            if (h < a.block) {
+#pragma unroll
+                for (int i = 0; i < DPL; i++) {
+                    if (i & h) continue;
+                    const float u = x[i], w = x[i + h];
+                    x[i] = u + w;
+                    x[i + h] = u - w;
+                }
+            }
+        }
+#pragma unroll
+        for (int st = 0; st < 2; st++) {
+            if ((DPL << st) < a.block) {
+                const int mask = 16 << st;
+                const bool upper = (lane & mask) != 0;
+#pragma unroll
+                for (int i = 0; i < DPL; i++) {
+                    const float o = __shfl_xor(x[i], mask, 64);
+                    x[i] = upper ? o - x[i] : x[i] + o;
+                }
+            }
+        }
+        float sum = 0.f, mx = 0.f;
+#pragma unroll
+        for (int i = 0; i < DPL; i++) {
+            x[i] *= a.cb;
+            sum += x[i];
+            mx = fmaxf(mx, fabsf(x[i]));
+        }
+        sum += __shfl_xor(sum, 16, 64);
+        sum += __shfl_xor(sum, 32, 64);
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const int E = __builtin_amdgcn_frexp_expf(mx); // mx < 2^E
+#pragma unroll
+        for (int j = 0; j < KS; j++) {
+            float y[8];
+#pragma unroll
+            for (int i = 0; i < 8; i++) y[i] = __builtin_ldexpf(x[8 * j + i], -E);
+            split_hilo(y, qhi[j], qlo[j]);
+        }
+        // score (log2 units) = Ar * s_K * acc + Br * z_K, acc = 2^-24 * sum(q 2^-E * code)
+        Ar = __builtin_ldexpf(a.scale_log2, 24 + E);
+        Br = a.scale_log2 * sum;
+#pragma unroll
+        for (int c = 0; c < NCB; c++) acc[c] = (float4_t){0.f, 0.f, 0.f, 0.f};
+    }
+
+    // INT4 page pair of unit step s (s >= n8): pages p0 + 2 (s - n8) and the next (clamped).
+    __device__ void load4(Buf<false>& b, int s) const
+    {
+        const int pi = p0 + 2 * (s - a.n8);
+        const int pa = mq_uniform(btrow + pi);
+        const int pb = mq_uniform(btrow + (pi + 1 < p1 ? pi + 1 : pi));
+        const uint8_t* A = a.pool + ((int64_t)pa * a.hkv + head) * a.page_block;
+        const uint8_t* B = a.pool + ((int64_t)pb * a.hkv + head) * a.page_block;
+        const int kslot = 8 * ((n >> 2) & 1) + (n & 3);
+        const uint8_t* kp = pick(n < 8, A, B) + kslot * 16;
+        const uint8_t* vp = pick(g < 2, A, B);
+        if constexpr (D == 128) {
+            kp += 256 * g;
+#pragma unroll
+            for (int t = 0; t < 2; t++) {
+                const u32x4 w = ld16(kp + 64 * t);
+#pragma unroll
+                for (int j = 0; j < 4; j++) b.k[t][j] = w[j];
+            }
+        } else {
+            kp += 256 * (g >> 1) + 8 * (g & 1);
+#pragma unroll
+            for (int t = 0; t < 2; t++) {
+                const u32x2 w = ld8(kp + 64 * t);
+                b.k[t][0] = w[0];
+                b.k[t][1] = w[1];
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < NCB; c++) b.v[c][0] = ld4(vp + 8 * D + (16 * c + n) * 8 + 4 * (g & 1));
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const u32x4 w = ld16(vp + 16 * D + 64 * (g & 1) + 16 * j);
+#pragma unroll
+            for (int i = 0; i < 4; i++) b.sc[4 * j + i] = w[i];
+        }
+    }
+
+    // Two INT8 tiles: ta (positions of the lane's key rows < 8) and tb.
+    __device__ void load8(Buf<true>& b, const uint8_t* A, const uint8_t* B) const
+    {
+        const int kslot = 8 * ((n >> 2) & 1) + (n & 3);
+        const uint8_t* kp = pick(n < 8, A, B) + IB * (g >> 1) + kslot * 16;
+        const uint8_t* vp = pick(g < 2, A, B);
+        if constexpr (D == 128) {
+            kp += 512 * (g & 1);
+#pragma unroll
+            for (int t = 0; t < 2; t++) {
+#pragma unroll
+                for (int c = 0; c < 2; c++) {
+                    const u32x4 w = ld16(kp + 64 * t + 256 * c);
+#pragma unroll
+                    for (int j = 0; j < 4; j++) b.k[t][4 * c + j] = w[j];
+                }
+            }
+        } else {
+            kp += 256 * (g & 1);
+#pragma unroll
+            for (int t = 0; t < 2; t++) {
+                const u32x4 w = ld16(kp + 64 * t);
+#pragma unroll
+                for (int j = 0; j < 4; j++) b.k[t][j] = w[j];
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < NCB; c++) {
+            const u32x2 w = ld8(vp + IB * (g & 1) + 8 * D + (16 * c + n) * 8);
+            b.v[c][0] = w[0];
+            b.v[c][1] = w[1];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const u32x4 w = ld16(vp + 16 * D + 64 * (g & 1) + 16 * j);
+#pragma unroll
+            for (int i = 0; i < 4; i++) b.sc[4 * j + i] = w[i];
+        }
+    }
+
+    __device__ void load8_step(Buf<true>& b, int s) const
+    {
+        if (FMT == FMT_INT8) {
+            const int pa = mq_uniform(btrow + 2 * s);
+            const int pb = mq_uniform(btrow + (2 * s + 1 < p1 ? 2 * s + 1 : 2 * s));
+            load8(b, a.pool + ((int64_t)pa * a.hkv + head) * a.page_block,
+                  a.pool + ((int64_t)pb * a.hkv + head) * a.page_block);
+        } else {
+            const int tb = 2 * s + 1 < a.int8_tiles ? 2 * s + 1 : 2 * s;
+            load8(b, t8 + (int64_t)(2 * s) * a.int8_tile, t8 + (int64_t)tb * a.int8_tile);
+        }
+    }
+
+    // Position of the lane's step element t (0..7) and whether this wave may read it at all.
+    template <bool IS8>
+    __device__ __forceinline__ void positions(int s, int (&pos)[8]) const
+    {
+        const int k0 = 8 * g;
+        if (!IS8) {
+            const int base = 16 * (p0 + 2 * (s - a.n8)) + k0;
+#pragma unroll
+            for (int t = 0; t < 8; t++) {
+                const int p = base + t;
+                pos[t] = (p >= lo4 && p < hi4) ? p : 0x7FFFFFFF;
+            }
+        } else if (FMT == FMT_INT8) {
+            const int base = 32 * s + k0;
+#pragma unroll
+            for (int t = 0; t < 8; t++) pos[t] = base + t < L ? base + t : 0x7FFFFFFF;
+        } else {
+            const int base = 32 * s + k0;
+#pragma unroll
+            for (int t = 0; t < 8; t++) {
+                const int u = base + t;
+                int p = 0x7FFFFFFF;
+                if (u < a.sinks) {
+                    p = u < L ? u : 0x7FFFFFFF;
+                } else if (u < a.sinks + a.recent) {
+                    int r = (u - a.sinks) - ring_mod;
+                    if (r < 0) r += a.recent;
+                    const int q = ring_base + r;
+                    p = q < L ? q : 0x7FFFFFFF;
+                }
+                pos[t] = p;
+            }
+        }
+    }
+
+    template <bool IS8>
+    __device__ void compute(const Buf<IS8>& b, int s)
+    {
+        int pos[8];
+        positions<IS8>(s, pos);
+        // S^T for the two tiles
+        float4_t sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < KS; j++) {
+            const u32x4 ka = IS8 ? spread_int8(b.k[0][2 * j], b.k[0][2 * j + 1]) : spread_int4(b.k[0][j]);
+            const u32x4 kb = IS8 ? spread_int8(b.k[1][2 * j], b.k[1][2 * j + 1]) : spread_int4(b.k[1][j]);
+            sa = mfma16x32(ka, qhi[j], sa);
+            sb = mfma16x32(kb, qhi[j], sb);
+            sa = mfma16x32(ka, qlo[j], sa);
+            sb = mfma16x32(kb, qlo[j], sb);
+        }
+        float st[8], w[8];
+        bool ok[8];
+        float wmax = -__builtin_inff();
+#pragma unroll
+        for (int t = 0; t < 8; t++) {
+            const float r = t < 4 ? sa[t] : sb[t - 4];
+            const uint32_t d0 = b.sc[2 * t], d1 = b.sc[2 * t + 1];
+            st[t] = fmaf(Ar * f16_bits_to_float(d0 & 0xFFFFu), r, Br * f16_bits_to_float(d0 >> 16));
+            ok[t] = pos[t] <= pos_r;
+            w[t] = ok[t] ? st[t] + (float)((d1 >> 10) & 31u) : -__builtin_inff();
+            wmax = fmaxf(wmax, w[t]);
+        }
+        wmax = fmaxf(wmax, __shfl_xor(wmax, 16, 64));
+        wmax = fmaxf(wmax, __shfl_xor(wmax, 32, 64));
+        const bool need = wmax > m_ref + kMqTau;
+        if (__builtin_amdgcn_ballot_w64(need)) {
+            const float f = need ? exp2f(m_ref - wmax) : 1.f;
+            if (need) m_ref = wmax;
+            lsum *= f;
+            zsum *= f;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const float fr = __shfl(f, 4 * g + i, 64);
+#pragma unroll
+                for (int c = 0; c < NCB; c++) acc[c][i] *= fr;
+            }
+        }
+        float P[8];
+#pragma unroll
+        for (int t = 0; t < 8; t++) {
+            const uint32_t d1 = b.sc[2 * t + 1];
+            // unread slots hold unspecified bytes (their scales may be inf / NaN): select, never
+            // multiply them by zero
+            const float p = ok[t] ? exp2f(st[t] - m_ref) : 0.f;
+            lsum += p;
+            zsum = ok[t] ? fmaf(p, f16_bits_to_float(d1 >> 16), zsum) : zsum;
+            P[t] = ok[t] ? p * (f16_bits_to_float(d1 & 0xFFFFu) * kPScale) : 0.f;
+        }
+        u32x4 phi, plo;
+        split_hilo(P, phi, plo);
+#pragma unroll
+        for (int c = 0; c < NCB; c++) {
+            const u32x4 bv = IS8 ? spread_int8(b.v[c][0], b.v[c][1]) : spread_int4(b.v[c][0]);
+            acc[c] = mfma16x32(phi, bv, acc[c]);
+            acc[c] = mfma16x32(plo, bv, acc[c]);
+        }
+    }
+
+    // INT8 steps [s0, s1): a few per task (the protection slots), one buffer.
+    __device__ void run8(int s0, int s1)
+    {
+        for (int s = s0; s < s1; s++) {
+            Buf<true> b;
+            load8_step(b, s);
+            compute<true>(b, s);
+        }
+    }
+
+    // INT4 steps [s0, s1) with the next step's loads in flight during each step; a load past the
+    // end repeats the last step's addresses and is not used.
+    __device__ void run4(int s0, int s1)
+    {
+        if (s0 >= s1) return;
+        Buf<false> b0, b1;
+        load4(b0, s0);
+        for (int s = s0; s < s1; s += 2) {
+            load4(b1, s + 1 < s1 ? s + 1 : s);
+            compute<false>(b0, s);
+            if (s + 1 >= s1) break;
+            load4(b0, s + 2 < s1 ? s + 2 : s + 1);
+            compute<false>(b1, s + 1);
+        }
+    }
+
+    __device__ void finish(int task)
+    {
+        lsum += __shfl_xor(lsum, 16, 64);
+        lsum += __shfl_xor(lsum, 32, 64);
+        zsum += __shfl_xor(zsum, 16, 64);
+        zsum += __shfl_xor(zsum, 32, 64);
+        if (g == 0) {
+            float* ml = a.part_ml + ((int64_t)task * kMqRows + n) * 2;
+            ml[0] = m_ref;
+            ml[1] = lsum;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int row = 4 * g + i;
+            const float z = __shfl(zsum, row, 64);
+            float* o = a.part_o + ((int64_t)task * kMqRows + row) * D + n;
+#pragma unroll
+            for (int c = 0; c < NCB; c++) o[16 * c] = fmaf(acc[c][i], 0.125f, z);
+        }
+    }
+};
+
+template <int D, int G, int FMT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void mq_split_kernel(MqArgs a)
+{
+    const int wave = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+    if (wave >= a.tasks) return;
+    const int lane = (int)(threadIdx.x & 63);
+    int lo = 0, hi = a.n_entries - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (mq_uniform(&a.entries[mid].task0) <= wave)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    MqEntry e;
+    e.seq = mq_uniform(&a.entries[lo].seq);
+    e.len = mq_uniform(&a.entries[lo].len);
+    e.nq = mq_uniform(&a.entries[lo].nq);
+    e.qrow0 = mq_uniform(&a.entries[lo].qrow0);
+    e.task0 = mq_uniform(&a.entries[lo].task0);
+    e.steps = mq_uniform(&a.entries[lo].steps);
+    e.nch = mq_uniform(&a.entries[lo].nch);
+    const int nrt = (e.nq * G + kMqRows - 1) / kMqRows;
+    int local = wave - e.task0;
+    const int head = local / (e.nch * nrt);
+    local -= head * e.nch * nrt;
+    const int chunk = local / nrt;
+    const int rt = local - chunk * nrt;
+
+    MqWave<D, G, FMT> W(a, lane);
+    W.seq = e.seq;
+    W.L = e.len;
+    W.head = head;
+    W.btrow = a.bt + (int64_t)e.seq * a.max_pps;
+    if (FMT == FMT_INT4_PROT) {
+        W.lo4 = a.sinks;
+        W.hi4 = e.len - a.recent;
+        W.p0 = a.sinks / kPageSize;
+        W.p1 = W.hi4 > W.lo4 ? (W.hi4 - 1) / kPageSize + 1 : W.p0;
+        W.ring_base = e.len - a.recent > a.sinks ? e.len - a.recent : a.sinks;
+        W.ring_mod = a.recent > 0 ? W.ring_base % a.recent : 0;
+        W.t8 = a.int8_pool + ((int64_t)e.seq * a.hkv + head) * a.int8_tiles * a.int8_tile;
+    } else {
+        W.lo4 = W.hi4 = W.p0 = W.ring_base = W.ring_mod = 0;
+        W.p1 = (e.len + kPageSize - 1) / kPageSize;
+        W.t8 = nullptr;
+    }
+    W.prologue(e, rt);
+    const int s0 = chunk * a.spc;
+    const int s1 = s0 + a.spc < e.steps ? s0 + a.spc : e.steps;
+    const int n8 = FMT == FMT_INT8 ? e.steps : a.n8;
+    W.run8(s0, s1 < n8 ? s1 : n8);
+    if (FMT == FMT_INT4_PROT) W.run4(s0 > n8 ? s0 : n8, s1);
+    W.finish(wave);
+}
+
+template <int D, int G, bool ROT>
+__global__ __launch_bounds__(256) void mq_merge_kernel(MqArgs a)
+{
+    constexpr int DPM = D / 64;
+    constexpr int QT = kMqRows / G;
+    const int wave = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+    if (wave >= a.groups * kMqRows) return;
+    const int lane = (int)(threadIdx.x & 63);
+    const int grp = wave / kMqRows, r = wave % kMqRows;
+    int lo = 0, hi = a.n_entries - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (mq_uniform(&a.entries[mid].grp0) <= grp)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    const int nq = mq_uniform(&a.entries[lo].nq);
+    const int qrow0 = mq_uniform(&a.entries[lo].qrow0);
+    const int task0 = mq_uniform(&a.entries[lo].task0);
+    const int grp0 = mq_uniform(&a.entries[lo].grp0);
+    const int nch = mq_uniform(&a.entries[lo].nch);
+    const int nrt = (nq * G + kMqRows - 1) / kMqRows;
+    const int local = grp - grp0;
+    const int head = local / nrt, rt = local - head * nrt;
+    const int jq = rt * QT + r / G, gi = r % G;
+    if (jq >= nq) return;
+    float M = -__builtin_inff();
+    for (int c = 0; c < nch; c++) {
+        const int64_t T = (int64_t)task0 + ((int64_t)head * nch + c) * nrt + rt;
+        M = fmaxf(M, mq_uniform(a.part_ml + (T * kMqRows + r) * 2));
+    }
+    float l = 0.f, o[DPM];
+#pragma unroll
+    for (int k = 0; k < DPM; k++) o[k] = 0.f;
+    for (int c = 0; c < nch; c++) {
+        const int64_t T = (int64_t)task0 + ((int64_t)head * nch + c) * nrt + rt;
+        const float m = mq_uniform(a.part_ml + (T * kMqRows + r) * 2);
+        const float lc = mq_uniform(a.part_ml + (T * kMqRows + r) * 2 + 1);
+        const float wgt = exp2f(m - M);
+        l = fmaf(wgt, lc, l);
+        const float* po = a.part_o + (T * kMqRows + r) * D + lane * DPM;
+#pragma unroll
+        for (int k = 0; k < DPM; k++) o[k] = fmaf(wgt, po[k], o[k]);
+    }
+    const float inv = 1.f / l;
+#pragma unroll
+    for (int k = 0; k < DPM; k++) o[k] *= inv;
+    if (ROT) {
+        // o H_bd (Sylvester H is symmetric, so this is also o H_bd^T), stages h = 1, 2, ..., b/2
+        if (DPM == 2 && a.block > 1) {
+            const float u = o[0], w = o[DPM - 1];
+            o[0] = u + w;
+            o[DPM - 1] = u - w;
+        }
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) {
+            if (m * DPM < a.block) {
+                const bool upper = (lane & m) != 0;
+#pragma unroll
+                for (int k = 0; k < DPM; k++) {
+                    const float other = __shfl_xor(o[k], m, 64);
+                    o[k] = upper ? other - o[k] : o[k] + other;
+                }
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < DPM; k++) o[k] *= a.cb;
+    }
+    float* out = a.out + ((int64_t)(qrow0 + jq) * a.hq + head * G + gi) * D + lane * DPM;
+#pragma unroll
+    for (int k = 0; k < DPM; k++) out[k] = o[k];
+}
+
+template <int D, int G, int FMT>
+hipError_t split_dispatch(const MqArgs& a, hipStream_t stream)
+{
+    const int blocks = (a.tasks + 3) / 4;
+    hipLaunchKernelGGL((mq_split_kernel<D, G, FMT>), dim3(blocks), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int D, int G>
+hipError_t merge_dispatch(const MqArgs& a, hipStream_t stream)
+{
+    const int64_t waves = (int64_t)a.groups * kMqRows;
+    const int blocks = (int)((waves + 3) / 4);
+    hipLaunchKernelGGL((mq_merge_kernel<D, G, true>), dim3(blocks), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int D, int G, int FMT>
+hipError_t split_residency(int* bpc)
+{
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(bpc, mq_split_kernel<D, G, FMT>, 256, 0);
+}
+
+} // namespace
+
+template <int FMT>
+hipError_t split_by_shape(int d, int g, const MqArgs& a, hipStream_t st)
+{
+    if (d == 128 && g == 4) return split_dispatch<128, 4, FMT>(a, st);
+    if (d == 128 && g == 2) return split_dispatch<128, 2, FMT>(a, st);
+    if (d == 128 && g == 1) return split_dispatch<128, 1, FMT>(a, st);
+    if (d == 64 && g == 4) return split_dispatch<64, 4, FMT>(a, st);
+    if (d == 64 && g == 2) return split_dispatch<64, 2, FMT>(a, st);
+    if (d == 64 && g == 1) return split_dispatch<64, 1, FMT>(a, st);
+    return hipErrorInvalidValue;
+}
+
+template <int FMT>
+hipError_t residency_by_shape(int d, int g, int* bpc)
+{
+    if (d == 128 && g == 4) return split_residency<128, 4, FMT>(bpc);
+    if (d == 128 && g == 2) return split_residency<128, 2, FMT>(bpc);
+    if (d == 128 && g == 1) return split_residency<128, 1, FMT>(bpc);
+    if (d == 64 && g == 4) return split_residency<64, 4, FMT>(bpc);
+    if (d == 64 && g == 2) return split_residency<64, 2, FMT>(bpc);
+    if (d == 64 && g == 1) return split_residency<64, 1, FMT>(bpc);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_mq_split(int d, int g, int format, const MqArgs& a, hipStream_t stream)
+{
+    if (a.tasks <= 0) return hipSuccess;
+    if (format == FMT_INT4_PROT) return split_by_shape<FMT_INT4_PROT>(d, g, a, stream);
+    if (format == FMT_INT8) return split_by_shape<FMT_INT8>(d, g, a, stream);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_mq_merge(int d, int g, const MqArgs& a, hipStream_t stream)
+{
+    if (a.groups <= 0) return hipSuccess;
+    if (d == 128 && g == 4) return merge_dispatch<128, 4>(a, stream);
+    if (d == 128 && g == 2) return merge_dispatch<128, 2>(a, stream);
+    if (d == 128 && g == 1) return merge_dispatch<128, 1>(a, stream);
+    if (d == 64 && g == 4) return merge_dispatch<64, 4>(a, stream);
+    if (d == 64 && g == 2) return merge_dispatch<64, 2>(a, stream);
+    if (d == 64 && g == 1) return merge_dispatch<64, 1>(a, stream);
+    return hipErrorInvalidValue;
+}
+
+hipError_t mq_split_residency(int d, int g, int format, int* blocks_per_cu)
+{
+    *blocks_per_cu = 0;
+    if (format == FMT_INT4_PROT) return residency_by_shape<FMT_INT4_PROT>(d, g, blocks_per_cu);
+    if (format == FMT_INT8) return residency_by_shape<FMT_INT8>(d, g, blocks_per_cu);
+    return hipSuccess;
+}
+
+} // namespace kv4

@@ -15,6 +15,7 @@
 #include <vector>
 
 #include "kv4_device_types.h"
+#include "kv4_mq_types.h"
 
 namespace kv4 {
 
@@ -116,6 +117,34 @@ inline int unit_steps(const Config& c, int L)
     if (c.format == FMT_INT8) return (pages + kInt8StepPages - 1) / kInt8StepPages;
     return pages; // bf16: one page per step
 }
+
+// Multi-query attention steps of one (sequence, kv head): INT4_PROT reads its INT8 protection
+// tiles two at a time, then the INT4 pages of [S, L - R) two at a time; the INT8 format reads its
+// pages two at a time.  (The BF16 format has no multi-query kernel.)
+inline int mq_int8_steps(const Config& c)
+{
+    if (c.format != FMT_INT4_PROT || c.sinks + c.recent == 0) return 0;
+    const int tiles = (c.sinks + c.recent + kPageSize - 1) / kPageSize;
+    return (tiles + 1) / 2;
+}
+
+inline int mq_unit_steps(const Config& c, int L)
+{
+    if (c.format == FMT_INT4_PROT) {
+        int p0, p1;
+        unit_int4_pages(c, L, &p0, &p1);
+        return mq_int8_steps(c) + (p1 - p0 + 1) / 2;
+    }
+    return ((L + kPageSize - 1) / kPageSize + 1) / 2;
+}
+
+struct MqPlan {
+    std::vector<MqEntry> entries;
+    int64_t tasks = 0;  // wave tasks of the split kernel
+    int64_t groups = 0; // (entry, kv head, row tile) groups; the merge runs 16 waves per group
+    int spc = 1;        // steps per chunk
+    int64_t rows = 0;   // query rows of the call (sum of n_q)
+};
 
 struct State {
     Config cfg;
@@ -244,6 +273,69 @@ struct State {
             }
         }
         *total = acc;
+        return OK;
+    }
+
+    // Multi-query plan: validates the call (ids distinct, 1 <= n_q[i] <= L) and splits every
+    // (entry, kv head, row tile) into chunks of `spc` steps, spc chosen so that the call has about
+    // `target_tasks` wave tasks.
+    Status plan_multi(int n_seqs, const int32_t* ids, const int32_t* n_q, int64_t target_tasks, MqPlan* plan,
+                      std::string* msg)
+    {
+        auto bad = [&](Status s, const char* m) {
+            if (msg) *msg = m;
+            return s;
+        };
+        if (cfg.format == FMT_BF16) return bad(UNSUPPORTED, "multi-query attention needs a quantized format");
+        if (n_seqs < 0) return bad(INVALID_ARGUMENT, "n_seqs < 0");
+        if (n_seqs > 0 && (!ids || !n_q)) return bad(INVALID_ARGUMENT, "null seq_ids / n_q");
+        std::vector<uint8_t> seen((size_t)cfg.max_seqs, 0);
+        for (int i = 0; i < n_seqs; i++) {
+            int s = ids[i];
+            if (s < 0 || s >= cfg.max_seqs) return bad(INVALID_ARGUMENT, "sequence id out of range");
+            if (seen[(size_t)s]) return bad(INVALID_ARGUMENT, "duplicate sequence id in one call");
+            seen[(size_t)s] = 1;
+            if (n_q[i] < 1) return bad(INVALID_ARGUMENT, "n_q < 1");
+            if (len[(size_t)s] < 1) return bad(SEQ_STATE, "attention over an empty sequence");
+            if (n_q[i] > len[(size_t)s]) return bad(SEQ_STATE, "n_q exceeds the sequence length");
+        }
+        const int G = cfg.hq / cfg.hkv;
+        int64_t work = 0, rows = 0;
+        for (int i = 0; i < n_seqs; i++) {
+            const int64_t nrt = ((int64_t)n_q[i] * G + kMqRows - 1) / kMqRows;
+            work += (int64_t)cfg.hkv * nrt * mq_unit_steps(cfg, len[(size_t)ids[i]]);
+            rows += n_q[i];
+        }
+        if (target_tasks < 1) target_tasks = 1;
+        int64_t spc = (work + target_tasks - 1) / target_tasks;
+        if (spc < 1) spc = 1;
+        plan->entries.clear();
+        int64_t tasks = 0, groups = 0, qrow = 0;
+        for (int i = 0; i < n_seqs; i++) {
+            const int L = len[(size_t)ids[i]];
+            const int steps = mq_unit_steps(cfg, L);
+            const int64_t nrt = ((int64_t)n_q[i] * G + kMqRows - 1) / kMqRows;
+            const int64_t nch = (steps + spc - 1) / spc;
+            MqEntry e;
+            e.seq = ids[i];
+            e.len = L;
+            e.nq = n_q[i];
+            e.qrow0 = (int32_t)qrow;
+            e.task0 = (int32_t)tasks;
+            e.grp0 = (int32_t)groups;
+            e.steps = steps;
+            e.nch = (int32_t)nch;
+            plan->entries.push_back(e);
+            tasks += (int64_t)cfg.hkv * nch * nrt;
+            groups += (int64_t)cfg.hkv * nrt;
+            qrow += n_q[i];
+            if (tasks >= ((int64_t)1 << 27) || qrow >= ((int64_t)1 << 30))
+                return bad(UNSUPPORTED, "multi-query call too large");
+        }
+        plan->tasks = tasks;
+        plan->groups = groups;
+        plan->spc = (int)spc;
+        plan->rows = rows;
         return OK;
     }
 };

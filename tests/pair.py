@@ -35,6 +35,12 @@ class Pair:
         torch.cuda.synchronize()
         return out.cpu().numpy().astype(np.float64), ref
 
+    def multi(self, seq_ids, n_q, q, scale=0.0):
+        out = self.gpu.multi_query_attention(seq_ids, n_q, q, scale=scale)
+        ref, _ = self.ora.attend_multi(seq_ids, n_q, bf16_bits(q), scale=scale)
+        torch.cuda.synchronize()
+        return out.cpu().numpy().astype(np.float64), ref
+
     def compare_cache(self, seqs):
         """Bit-exact comparison of page ids, codes and scales (valid slots only).  Returns the number
         of compared (slot, kv, head) records."""

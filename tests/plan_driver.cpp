@@ -13,6 +13,8 @@
 //   decode n id0 id1 ...         -> "status S total T", then one "unit seq len entry head step_begin"
 //                                   line per unit, then "end"
 //   sizes                        -> "sizes page_pool int8_pool block_table page_block int8_tile int8_tiles"
+//   multi target n id0 nq0 ...   -> "status S tasks T groups G spc C n8 N8", then one
+//                                   "entry seq len nq qrow0 task0 grp0 steps nch" line per entry, "end"
 #include <cstdio>
 #include <iostream>
 #include <sstream>
@@ -69,6 +71,21 @@ int main()
             std::printf("\n");
         } else if (cmd == "freepages") {
             std::printf("free %d\n", (int)st.free_list.size());
+        } else if (cmd == "multi") {
+            long long target = 0;
+            int n = 0;
+            in >> target >> n;
+            std::vector<int32_t> ids(n > 0 ? n : 0), nq(n > 0 ? n : 0);
+            for (int i = 0; i < n; i++) in >> ids[i] >> nq[i];
+            kv4::MqPlan plan;
+            kv4::Status s = st.plan_multi(n, ids.data(), nq.data(), target, &plan, nullptr);
+            std::printf("status %d tasks %lld groups %lld spc %d n8 %d\n", (int)s, (long long)plan.tasks,
+                        (long long)plan.groups, plan.spc, kv4::mq_int8_steps(st.cfg));
+            if (s == kv4::OK)
+                for (const auto& e : plan.entries)
+                    std::printf("entry %d %d %d %d %d %d %d %d\n", e.seq, e.len, e.nq, e.qrow0, e.task0, e.grp0, e.steps,
+                                e.nch);
+            std::printf("end\n");
         } else if (cmd == "decode") {
             int n = 0;
             in >> n;

@@ -1,0 +1,155 @@
+"""Multi-query attention: the host planner's work split and the kernel's position arithmetic,
+checked on the CPU before any launch.
+
+The planner runs through the host-only driver program.  The kernel's mapping from (wave task,
+step, lane element) to a cache position is mirrored here line for line from kv4_mq.hip, and the
+test checks that every query row attends exactly positions 0 .. its own position, each once,
+from the copy decode reads at length L (INT8 slot when protected, INT4 page otherwise), and that
+every page and INT8 tile index the kernel forms stays inside the sequence's buffers.
+"""
+import math
+
+import pytest
+
+import oracle
+from tests.test_host_abi import Planner, driver  # noqa: F401  (fixture)
+
+P = 16
+
+
+def _plan(pl, target, calls):
+    line = "multi %d %d " % (target, len(calls)) + " ".join("%d %d" % c for c in calls)
+    first, rows = pl.cmd(line, block=True)
+    st = dict(zip(first[0::2], (int(x) for x in first[1::2])))
+    return st, rows
+
+
+def _positions(kind, s, k, L, S, R, n8, fmt):
+    """Position of step element k (0..31) of unit step s, or None (kv4_mq.hip: positions())."""
+    if kind == "int4":
+        p0 = S // P
+        p = P * (p0 + 2 * (s - n8)) + k
+        return p if S <= p < L - R else None
+    if fmt == 1:
+        p = 32 * s + k
+        return p if p < L else None
+    u = 32 * s + k
+    if u < S:
+        return u if u < L else None
+    if u < S + R:
+        base = max(S, L - R)
+        r = (u - S) - base % R
+        if r < 0:
+            r += R
+        q = base + r
+        return q if q < L else None
+    return None
+
+
+def _emulate(st, entries, hq, hkv, S, R, fmt):
+    G = hq // hkv
+    QT = 16 // G
+    spc, n8 = st["spc"], st["n8"]
+    seen = {}
+    task0s = [e[4] for e in entries]
+    for w in range(st["tasks"]):
+        ei = max(i for i, t0 in enumerate(task0s) if t0 <= w)
+        seq, L, nq, qrow0, task0, grp0, steps, nch = entries[ei]
+        nrt = -(-nq * G // 16)
+        local = w - task0
+        head = local // (nch * nrt)
+        local -= head * nch * nrt
+        chunk, rt = divmod(local, nrt)
+        assert 0 <= head < hkv and 0 <= chunk < nch
+        s0 = chunk * spc
+        s1 = min(s0 + spc, steps)
+        assert s0 < s1
+        n8e = steps if fmt == 1 else n8
+        kinds = [("int8", s) for s in range(s0, min(s1, n8e))] + [("int4", s) for s in range(max(s0, n8e), s1)]
+        if fmt == 1:
+            assert all(k == "int8" for k, _ in kinds)
+        for kind, s in kinds:
+            # buffer indices the kernel forms (clamped second page / tile)
+            if kind == "int4":
+                p0 = S // P
+                p1 = (L - R - 1) // P + 1
+                pi = p0 + 2 * (s - n8)
+                assert p0 <= pi < p1 <= math.ceil(L / P)
+            elif fmt == 1:
+                assert 2 * s < math.ceil(L / P)
+            else:
+                assert 2 * s < math.ceil((S + R) / P)
+            for k in range(32):
+                pos = _positions(kind, s, k, L, S, R, n8, fmt)
+                if pos is None:
+                    continue
+                if kind == "int8" and fmt == 0:
+                    assert oracle.int8_slot(pos, S, R) == 32 * s + k
+                for r in range(16):
+                    jq = rt * QT + r // G
+                    if jq >= nq:
+                        continue
+                    pos_r = L - nq + jq
+                    if pos <= pos_r:
+                        key = (ei, head, jq, r % G)
+                        seen.setdefault(key, []).append((pos, kind))
+    return seen
+
+
+@pytest.mark.parametrize("hq,hkv,S,R,fmt,lens,nqs,target", [
+    (32, 8, 4, 128, 0, [1, 17, 132, 133, 300, 700], [1, 5, 16, 40, 133, 150], 64),
+    (32, 8, 4, 128, 0, [700, 2000], [3, 1], 4096),
+    (8, 2, 4, 32, 0, [36, 37, 90, 500], [36, 7, 90, 64], 7),
+    (4, 4, 0, 0, 0, [1, 15, 16, 17, 400], [1, 15, 2, 17, 33], 16),
+    (16, 8, 4, 0, 0, [3, 50, 260], [3, 20, 11], 9),
+    (16, 8, 0, 40, 0, [39, 40, 41, 300], [39, 12, 41, 100], 30),
+    (8, 4, 0, 0, 1, [1, 31, 32, 33, 500], [1, 31, 5, 33, 77], 12),
+])
+def test_rows_attend_each_position_once_from_the_right_copy(driver, hq, hkv, S, R, fmt, lens, nqs, target):
+    pl = Planner(driver)
+    try:
+        first, _ = pl.cmd("init %d %d 128 16 4096 16 512 %d %d 128 %d" % (hq, hkv, S, R, fmt))
+        assert first == ["status", "0"]
+        for i, L in enumerate(lens):
+            first, _ = pl.cmd("append 1 %d %d" % (i, L), block=True)
+            assert first == ["status", "0"]
+        st, entries = _plan(pl, target, list(enumerate(nqs)))
+        assert st["status"] == 0
+        G = hq // hkv
+        assert st["groups"] == sum(hkv * -(-nq * G // 16) for nq in nqs)
+        seen = _emulate(st, entries, hq, hkv, S, R, fmt)
+        for ei, (L, nq) in enumerate(zip(lens, nqs)):
+            for h in range(hkv):
+                for jq in range(nq):
+                    for gi in range(G):
+                        got = sorted(seen.get((ei, h, jq, gi), []))
+                        pos_r = L - nq + jq
+                        assert [p for p, _ in got] == list(range(pos_r + 1)), (ei, h, jq, gi)
+                        for p, kind in got:
+                            want = "int8" if (fmt == 1 or _prot(p, L, S, R)) else "int4"
+                            assert kind == want, (p, L)
+    finally:
+        pl.close()
+
+
+def _prot(t, L, S, R):
+    return t < min(S, L) or max(S, L - R) <= t < L
+
+
+def test_multi_plan_errors(driver):
+    pl = Planner(driver)
+    try:
+        assert pl.cmd("init 8 2 64 16 256 8 64 4 32 64 0")[0] == ["status", "0"]
+        assert pl.cmd("append 2 0 10 1 40", block=True)[0] == ["status", "0"]
+        assert _plan(pl, 100, [(0, 11)])[0]["status"] == 3   # n_q > L
+        assert _plan(pl, 100, [(0, 0)])[0]["status"] == 1    # n_q < 1
+        assert _plan(pl, 100, [(2, 1)])[0]["status"] == 3    # empty sequence
+        assert _plan(pl, 100, [(0, 1), (0, 1)])[0]["status"] == 1
+        assert _plan(pl, 100, [(9, 1)])[0]["status"] == 1
+        st, rows = _plan(pl, 100, [])
+        assert st["status"] == 0 and st["tasks"] == 0 and rows == []
+        assert pl.cmd("init 8 2 64 16 256 8 64 4 32 1 2")[0] == ["status", "0"]
+        assert pl.cmd("append 1 0 10", block=True)[0] == ["status", "0"]
+        assert _plan(pl, 100, [(0, 1)])[0]["status"] == 5    # BF16: unsupported
+    finally:
+        pl.close()
