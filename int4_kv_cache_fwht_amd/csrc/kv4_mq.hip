@@ -13,8 +13,8 @@
 //                 code * 2^-24, exact); the B operand the rotated query rows, scaled by a power of
 //                 two and split into hi + lo fp16.  A score is s_K (q . code) + z_K sum(q).
 //   O += P' V:    the A operand is p * s_V (hi + lo fp16), the B operand the value codes, which
-//                 the page stores dim-major, again as subnormal patterns; sum_t p_t z_V,t is
-//                 accumulated per lane.
+//                 the page stores dim-major, centred (code - 8; INT8: - 128) as fp16 integers;
+//                 sum_t p_t (z_V,t + 8 s_V,t) is accumulated per lane.
 // Positions are assigned to the S^T rows so that the accumulator of lane l holds the scores of
 // query row l % 16 for 8 consecutive positions of the step -- exactly the positions whose p * s_V
 // lane l supplies to the PV operand, and whose value codes are one 4-byte (INT4) or 8-byte (INT8)
@@ -45,8 +45,8 @@ __device__ __forceinline__ float4_t mfma16x32(u32x4 a, u32x4 b, float4_t c)
                                                   0, 0, 0);
 }
 
-// Eight INT4 codes, nibble i = element i, as fp16 subnormal patterns in the element order
-// (0, 4, 1, 5, 2, 6, 3, 7).
+// Eight INT4 codes, nibble i = element i, one per 16-bit half in the element order
+// (0, 4, 1, 5, 2, 6, 3, 7); as fp16 these are the subnormal patterns code * 2^-24 (exact).
 __device__ __forceinline__ u32x4 spread_int4(uint32_t w)
 {
     return (u32x4){w & 0x000F000Fu, (w >> 4) & 0x000F000Fu, (w >> 8) & 0x000F000Fu, (w >> 12) & 0x000F000Fu};
@@ -57,6 +57,25 @@ __device__ __forceinline__ u32x4 spread_int8(uint32_t w0, uint32_t w1)
 {
     return (u32x4){__builtin_amdgcn_perm(w1, w0, 0x0C040C00u), __builtin_amdgcn_perm(w1, w0, 0x0C050C01u),
                    __builtin_amdgcn_perm(w1, w0, 0x0C060C02u), __builtin_amdgcn_perm(w1, w0, 0x0C070C03u)};
+}
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+// Spread value codes (code in the low bits of each half) -> code - MID as fp16 integers, MID = 8
+// (INT4) or 128 (INT8): 0x6400 | code is the fp16 value 1024 + code, and one packed fp16
+// subtraction of 1024 + MID is exact.  Centred codes keep the PV accumulators at the scale of the
+// result: with raw codes they would hold about sum p (s_V * code midpoint), which the zero-point
+// term then cancels, and the MFMA accumulation error of that large sum showed in the output at
+// the 1e-4 level.  (The score path has no such cancellation; its key codes stay raw.)
+template <int MID>
+__device__ __forceinline__ u32x4 centre(u32x4 x)
+{
+    const half2_t off = {(_Float16)(-(1024 + MID)), (_Float16)(-(1024 + MID))};
+    u32x4 r;
+#pragma unroll
+    for (int s = 0; s < 4; s++)
+        r[s] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, x[s] | 0x64006400u) + off);
+    return r;
 }
 
 // hi + lo fp16 of eight floats, same element order as the spreads.
@@ -100,6 +119,7 @@ struct MqWave {
     const MqArgs& a;
     const int lane, n, g;
     int seq, L, head, pos_r;
+    int first_pos;       // position of the row tile's first query (wave-uniform)
     int lo4, hi4;        // INT4_PROT: INT4-read positions [S, L - R)
     int ring_base, ring_mod; // INT4_PROT: first recent position and its residue mod R
     const uint8_t* t8;   // INT4_PROT: this (sequence, kv head)'s INT8 tiles
@@ -117,6 +137,7 @@ struct MqWave {
         const int jq = rt * QT + n / G, gi = n % G;
         const bool row_ok = jq < e.nq;
         pos_r = row_ok ? e.len - e.nq + jq : -1;
+        first_pos = e.len - e.nq + rt * QT;
         const uint16_t* qp = a.q + ((int64_t)(e.qrow0 + (row_ok ? jq : 0)) * a.hq + head * G + gi) * D + DPL * g;
         float x[DPL];
 #pragma unroll
@@ -172,7 +193,7 @@ struct MqWave {
             for (int i = 0; i < 8; i++) y[i] = __builtin_ldexpf(x[8 * j + i], -E);
             split_hilo(y, qhi[j], qlo[j]);
         }
-        // score (log2 units) = Ar * s_K * acc + Br * z_K, acc = 2^-24 * sum(q 2^-E * code)
+        // score (log2 units) = Ar * s_K * acc + Br * z_K, acc = 2^-24 sum(q 2^-E * code)
         Ar = __builtin_ldexpf(a.scale_log2, 24 + E);
         Br = a.scale_log2 * sum;
 #pragma unroll
@@ -305,11 +326,14 @@ struct MqWave {
         }
     }
 
-    template <bool IS8>
+    // One step.  FULL: every position of the step is readable and at or before every row's own
+    // position (wave-uniform), so no per-position test is made.
+    template <bool IS8, bool FULL>
     __device__ void compute(const Buf<IS8>& b, int s)
     {
+        constexpr int MID = IS8 ? 128 : 8;
         int pos[8];
-        positions<IS8>(s, pos);
+        if (!FULL) positions<IS8>(s, pos);
         // S^T for the two tiles
         float4_t sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -328,8 +352,9 @@ struct MqWave {
         for (int t = 0; t < 8; t++) {
             const float r = t < 4 ? sa[t] : sb[t - 4];
             const uint32_t d0 = b.sc[2 * t], d1 = b.sc[2 * t + 1];
-            st[t] = fmaf(Ar * f16_bits_to_float(d0 & 0xFFFFu), r, Br * f16_bits_to_float(d0 >> 16));
-            ok[t] = pos[t] <= pos_r;
+            const float sK = f16_bits_to_float(d0 & 0xFFFFu);
+            st[t] = fmaf(Ar * sK, r, Br * f16_bits_to_float(d0 >> 16));
+            ok[t] = FULL || pos[t] <= pos_r;
             w[t] = ok[t] ? st[t] + (float)((d1 >> 10) & 31u) : -__builtin_inff();
             wmax = fmaxf(wmax, w[t]);
         }
@@ -337,7 +362,7 @@ struct MqWave {
         wmax = fmaxf(wmax, __shfl_xor(wmax, 32, 64));
         const bool need = wmax > m_ref + kMqTau;
         if (__builtin_amdgcn_ballot_w64(need)) {
-            const float f = need ? exp2f(m_ref - wmax) : 1.f;
+            const float f = need ? __builtin_amdgcn_exp2f(m_ref - wmax) : 1.f;
             if (need) m_ref = wmax;
             lsum *= f;
             zsum *= f;
@@ -354,16 +379,17 @@ struct MqWave {
             const uint32_t d1 = b.sc[2 * t + 1];
             // unread slots hold unspecified bytes (their scales may be inf / NaN): select, never
             // multiply them by zero
-            const float p = ok[t] ? exp2f(st[t] - m_ref) : 0.f;
+            const float p = ok[t] ? __builtin_amdgcn_exp2f(st[t] - m_ref) : 0.f;
             lsum += p;
-            zsum = ok[t] ? fmaf(p, f16_bits_to_float(d1 >> 16), zsum) : zsum;
-            P[t] = ok[t] ? p * (f16_bits_to_float(d1 & 0xFFFFu) * kPScale) : 0.f;
+            const float sV = f16_bits_to_float(d1 & 0xFFFFu);
+            zsum = ok[t] ? fmaf(p, fmaf((float)MID, sV, f16_bits_to_float(d1 >> 16)), zsum) : zsum;
+            P[t] = ok[t] ? p * (sV * kPScale) : 0.f;
         }
         u32x4 phi, plo;
         split_hilo(P, phi, plo);
 #pragma unroll
         for (int c = 0; c < NCB; c++) {
-            const u32x4 bv = IS8 ? spread_int8(b.v[c][0], b.v[c][1]) : spread_int4(b.v[c][0]);
+            const u32x4 bv = centre<MID>(IS8 ? spread_int8(b.v[c][0], b.v[c][1]) : spread_int4(b.v[c][0]));
             acc[c] = mfma16x32(phi, bv, acc[c]);
             acc[c] = mfma16x32(plo, bv, acc[c]);
         }
@@ -375,8 +401,24 @@ struct MqWave {
         for (int s = s0; s < s1; s++) {
             Buf<true> b;
             load8_step(b, s);
-            compute<true>(b, s);
+            compute<true, false>(b, s);
         }
+    }
+
+    // INT4 step s covers positions [16 (p0 + 2 (s - n8)), +32): all readable and not after the
+    // tile's first row (the smallest row position)?
+    __device__ __forceinline__ bool interior(int s) const
+    {
+        const int base = kPageSize * (p0 + 2 * (s - a.n8));
+        return base >= lo4 && base + kMqStepSlots <= hi4 && base + kMqStepSlots - 1 <= first_pos;
+    }
+
+    __device__ __forceinline__ void step4(const Buf<false>& b, int s)
+    {
+        if (interior(s))
+            compute<false, true>(b, s);
+        else
+            compute<false, false>(b, s);
     }
 
     // INT4 steps [s0, s1) with the next step's loads in flight during each step; a load past the
@@ -388,10 +430,10 @@ struct MqWave {
         load4(b0, s0);
         for (int s = s0; s < s1; s += 2) {
             load4(b1, s + 1 < s1 ? s + 1 : s);
-            compute<false>(b0, s);
+            step4(b0, s);
             if (s + 1 >= s1) break;
             load4(b0, s + 2 < s1 ? s + 2 : s + 1);
-            compute<false>(b1, s + 1);
+            step4(b1, s + 1);
         }
     }
 
@@ -412,7 +454,7 @@ struct MqWave {
             const float z = __shfl(zsum, row, 64);
             float* o = a.part_o + ((int64_t)task * kMqRows + row) * D + n;
 #pragma unroll
-            for (int c = 0; c < NCB; c++) o[16 * c] = fmaf(acc[c][i], 0.125f, z);
+            for (int c = 0; c < NCB; c++) o[16 * c] = fmaf(acc[c][i], 1.f / kPScale, z);
         }
     }
 };
