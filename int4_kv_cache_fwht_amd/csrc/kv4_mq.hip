@@ -90,6 +90,22 @@ __device__ __forceinline__ void split_hilo(const float (&x)[8], u32x4& hi, u32x4
     }
 }
 
+// hi + lo fp16 of eight floats (same element order), hi truncated toward zero: the residual
+// x - hi is exact in fp32 and its own fp16 truncation leaves about 2^-20 of x.
+__device__ __forceinline__ void split_hilo_rtz(const float (&x)[8], u32x4& hi, u32x4& lo)
+{
+#pragma unroll
+    for (int s = 0; s < 4; s++) {
+        const half2_t h = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(x[s], x[s + 4]));
+        const float r0 = fmaf((float)h[0], -1.f, x[s]), r1 = fmaf((float)h[1], -1.f, x[s + 4]);
+        hi[s] = __builtin_bit_cast(uint32_t, h);
+        lo[s] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(r0, r1));
+    }
+}
+
+__device__ __forceinline__ float lo_half(uint32_t d) { return (float)__builtin_bit_cast(half2_t, d)[0]; }
+__device__ __forceinline__ float hi_half(uint32_t d) { return (float)__builtin_bit_cast(half2_t, d)[1]; }
+
 __device__ __forceinline__ u32x4 ld16(const uint8_t* p) { return *(const u32x4*)p; }
 __device__ __forceinline__ u32x2 ld8(const uint8_t* p) { return *(const u32x2*)p; }
 __device__ __forceinline__ uint32_t ld4(const uint8_t* p) { return *(const uint32_t*)p; }
@@ -345,6 +361,7 @@ struct MqWave {
             sa = mfma16x32(ka, qlo[j], sa);
             sb = mfma16x32(kb, qlo[j], sb);
         }
+        // fp16 scales enter the fp32 arithmetic as fma operands (v_fma_mix_f32: no conversions)
         float st[8], w[8];
         bool ok[8];
         float wmax = -__builtin_inff();
@@ -352,8 +369,7 @@ struct MqWave {
         for (int t = 0; t < 8; t++) {
             const float r = t < 4 ? sa[t] : sb[t - 4];
             const uint32_t d0 = b.sc[2 * t], d1 = b.sc[2 * t + 1];
-            const float sK = f16_bits_to_float(d0 & 0xFFFFu);
-            st[t] = fmaf(Ar * sK, r, Br * f16_bits_to_float(d0 >> 16));
+            st[t] = fmaf(lo_half(d0), r * Ar, fmaf(hi_half(d0), Br, 0.f));
             ok[t] = FULL || pos[t] <= pos_r;
             w[t] = ok[t] ? st[t] + (float)((d1 >> 10) & 31u) : -__builtin_inff();
             wmax = fmaxf(wmax, w[t]);
@@ -373,20 +389,22 @@ struct MqWave {
                 for (int c = 0; c < NCB; c++) acc[c][i] *= fr;
             }
         }
+        // p is carried as p * 2^27 (lsum, zsum too; undone in finish): P = p * 2^27 * s_V is then
+        // one fma, and P < 2^14 by the reference rule
         float P[8];
+        const float m27 = m_ref - 27.f;
 #pragma unroll
         for (int t = 0; t < 8; t++) {
             const uint32_t d1 = b.sc[2 * t + 1];
             // unread slots hold unspecified bytes (their scales may be inf / NaN): select, never
             // multiply them by zero
-            const float p = ok[t] ? __builtin_amdgcn_exp2f(st[t] - m_ref) : 0.f;
+            const float p = ok[t] ? __builtin_amdgcn_exp2f(st[t] - m27) : 0.f;
             lsum += p;
-            const float sV = f16_bits_to_float(d1 & 0xFFFFu);
-            zsum = ok[t] ? fmaf(p, fmaf((float)MID, sV, f16_bits_to_float(d1 >> 16)), zsum) : zsum;
-            P[t] = ok[t] ? p * (sV * kPScale) : 0.f;
+            zsum = ok[t] ? fmaf(p, fmaf(lo_half(d1), (float)MID, hi_half(d1)), zsum) : zsum;
+            P[t] = ok[t] ? fmaf(lo_half(d1), p, 0.f) : 0.f;
         }
         u32x4 phi, plo;
-        split_hilo(P, phi, plo);
+        split_hilo_rtz(P, phi, plo);
 #pragma unroll
         for (int c = 0; c < NCB; c++) {
             const u32x4 bv = centre<MID>(IS8 ? spread_int8(b.v[c][0], b.v[c][1]) : spread_int4(b.v[c][0]));
@@ -446,7 +464,7 @@ struct MqWave {
         if (g == 0) {
             float* ml = a.part_ml + ((int64_t)task * kMqRows + n) * 2;
             ml[0] = m_ref;
-            ml[1] = lsum;
+            ml[1] = lsum * (1.f / kPScale);
         }
 #pragma unroll
         for (int i = 0; i < 4; i++) {
@@ -454,7 +472,7 @@ struct MqWave {
             const float z = __shfl(zsum, row, 64);
             float* o = a.part_o + ((int64_t)task * kMqRows + row) * D + n;
 #pragma unroll
-            for (int c = 0; c < NCB; c++) o[16 * c] = fmaf(acc[c][i], 1.f / kPScale, z);
+            for (int c = 0; c < NCB; c++) o[16 * c] = (acc[c][i] + z) * (1.f / kPScale);
         }
     }
 };
