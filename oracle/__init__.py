@@ -104,6 +104,8 @@ def lib():
         L.kv4o_dequant_seq.restype = c_int
         L.kv4o_decode.argtypes = [P, c_int, P, P, c_double, P, c_int, P]
         L.kv4o_decode.restype = c_int
+        L.kv4o_set_eviction.argtypes = [P, c_int]
+        L.kv4o_set_eviction.restype = c_int
         L.kv4o_attend_multi.argtypes = [P, c_int, P, P, P, c_double, P, c_int, P]
         L.kv4o_attend_multi.restype = c_int
         _lib = L
@@ -206,7 +208,7 @@ class OracleCache:
 
     def __init__(self, num_q_heads: int, num_kv_heads: int, head_dim: int, page_size: int, num_pages: int,
                  max_seqs: int, max_pages_per_seq: int, num_sinks: int, num_recent: int, hadamard_block: int,
-                 fmt: int = FMT_INT4_PROT):
+                 fmt: int = FMT_INT4_PROT, eviction: int = 0):
         self.hq, self.hkv, self.d = num_q_heads, num_kv_heads, head_dim
         self.P, self.num_pages, self.max_seqs, self.max_pps = page_size, num_pages, max_seqs, max_pages_per_seq
         self.S, self.R, self.b, self.fmt = num_sinks, num_recent, hadamard_block, fmt
@@ -215,6 +217,9 @@ class OracleCache:
         if not h:
             raise ValueError("invalid oracle cache configuration")
         self._h = ctypes.c_void_p(h)
+        self.eviction = eviction
+        if eviction and lib().kv4o_set_eviction(self._h, int(eviction)) != OK:
+            raise ValueError("invalid eviction rule for this format")
 
     def close(self):
         if self._h:

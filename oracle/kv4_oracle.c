@@ -298,6 +298,7 @@ int kv4o_int8_slot(int t, int S, int R)
 
 typedef struct kv4o_cache {
     int hq, hkv, d, P, num_pages, max_seqs, max_pps, S, R, b, fmt;
+    int requant; /* eviction rule: 0 dual write, 1 INT4 codes from the INT8 round trip */
     int* len;  /* [max_seqs] */
     int* bt;   /* [max_seqs][max_pps] */
     int* fifo; /* circular free list of capacity num_pages */
@@ -397,6 +398,23 @@ kv4o_cache* kv4o_create(int hq, int hkv, int d, int P, int num_pages, int max_se
     return c;
 }
 
+/* Selects the INT8 -> INT4 eviction rule (INT4_PROT only; before the first append).
+ *   0: dual write -- a position's INT4 code is quantized from its rotated values when appended.
+ *   1: re-quantization -- a position that leaves the recent window moves from INT8 to INT4 by
+ *      quantizing its INT8 copy's dequantized row ([KV4]: tokens leaving the window move from
+ *      INT8 to INT4).  That row depends on the position alone, so the INT4 code is computed when
+ *      the position is appended (for every position, so that a prefill equals single appends). */
+int kv4o_set_eviction(kv4o_cache* c, int mode)
+{
+    if (mode < 0 || mode > 1 || (mode == 1 && c->fmt != KV4O_FMT_INT4_PROT))
+        return KV4O_INVALID_ARGUMENT;
+    for (int i = 0; i < c->max_seqs; i++)
+        if (c->len[i] != 0)
+            return KV4O_SEQ_STATE;
+    c->requant = mode;
+    return KV4O_OK;
+}
+
 static int fifo_pop(kv4o_cache* c)
 {
     int p = c->fifo[c->fifo_head];
@@ -461,9 +479,14 @@ static int write_token(kv4o_cache* c, int seq, int t, int L_new, const uint16_t*
     int slot = t % c->P;
     if (!k || !v)
         return KV4O_OK;
-    float* y = (float*)malloc((size_t)c->d * sizeof(float));
-    if (!y)
+    float* y = (float*)malloc((size_t)c->d * 2 * sizeof(float));
+    uint8_t* c8row = (uint8_t*)malloc((size_t)c->d);
+    if (!y || !c8row) {
+        free(y);
+        free(c8row);
         return KV4O_INVALID_ARGUMENT;
+    }
+    float* x8 = y + c->d;
     int rc = KV4O_OK;
     for (int h = 0; h < c->hkv && rc == KV4O_OK; h++) {
         for (int kv = 0; kv < 2 && rc == KV4O_OK; kv++) {
@@ -475,7 +498,23 @@ static int write_token(kv4o_cache* c, int seq, int t, int L_new, const uint16_t*
             }
             kv4o_rotate_bf16(x, c->d, c->b, y);
             int Q = (c->fmt == KV4O_FMT_INT8) ? 255 : 15;
-            if (kv4o_quantize(y, c->d, Q, c->codes + pi * c->d, &c->sz[pi * 2], &c->sz[pi * 2 + 1]) != 0) {
+            if (c->requant) {
+                /* INT4 from the INT8 round trip: x8 = fl32(s8 * code8 + z8) (the product is exact) */
+                uint16_t s8b, z8b;
+                if (kv4o_quantize(y, c->d, 255, c8row, &s8b, &z8b) != 0) {
+                    rc = KV4O_PRECONDITION;
+                    break;
+                }
+                float s8f = (float)kv4o_fp16_value(s8b), z8f = (float)kv4o_fp16_value(z8b);
+                for (int i = 0; i < c->d; i++) {
+                    float prod = s8f * (float)c8row[i];
+                    x8[i] = prod + z8f;
+                }
+                if (kv4o_quantize(x8, c->d, 15, c->codes + pi * c->d, &c->sz[pi * 2], &c->sz[pi * 2 + 1]) != 0) {
+                    rc = KV4O_PRECONDITION;
+                    break;
+                }
+            } else if (kv4o_quantize(y, c->d, Q, c->codes + pi * c->d, &c->sz[pi * 2], &c->sz[pi * 2 + 1]) != 0) {
                 rc = KV4O_PRECONDITION;
                 break;
             }
@@ -491,6 +530,7 @@ static int write_token(kv4o_cache* c, int seq, int t, int L_new, const uint16_t*
         }
     }
     free(y);
+    free(c8row);
     if (rc == KV4O_OK)
         c->filled[(size_t)page * c->P + slot] = 1;
     return rc;
