@@ -239,15 +239,16 @@ def cpu_baseline(w, seconds, device):
 
 
 QUALITY_VARIANTS = [
-    # name, format, hadamard block (0 = workload's), sinks, recent (None = workload's)
-    ("int4_rot_prot", "int4", 0, None, None),
-    ("int4_rot_noprot", "int4", 0, 0, 0),
-    ("int4_norot_prot", "int4", 1, None, None),
-    ("int4_rot_sinks_only", "int4", 0, None, 0),
-    ("int4_rot_recent_only", "int4", 0, 0, None),
-    ("int4_plain", "int4", 1, 0, 0),
-    ("int8", "int8", 0, 0, 0),
-    ("bf16", "bf16", 1, 0, 0),
+    # name, format, hadamard block (0 = workload's), sinks, recent (None = workload's), eviction
+    ("int4_rot_prot", "int4", 0, None, None, 0),
+    ("int4_rot_prot_requant", "int4", 0, None, None, 1),
+    ("int4_rot_noprot", "int4", 0, 0, 0, 0),
+    ("int4_norot_prot", "int4", 1, None, None, 0),
+    ("int4_rot_sinks_only", "int4", 0, None, 0, 0),
+    ("int4_rot_recent_only", "int4", 0, 0, None, 0),
+    ("int4_plain", "int4", 1, 0, 0, 0),
+    ("int8", "int8", 0, 0, 0, 0),
+    ("bf16", "bf16", 1, 0, 0, 0),
 ]
 
 
@@ -274,12 +275,12 @@ def quality(w, device, n_seqs=4):
             p_ = np.exp(e - e.max())
             ref[i, g] = (p_ / p_.sum()) @ vf[:, g // G, :]
     res = {}
-    for name, fmt, block, S, R in QUALITY_VARIANTS:
+    for name, fmt, block, S, R, evict in QUALITY_VARIANTS:
         cfg = kv4.Config(num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
                          num_pages=sum(math.ceil(L / 16) for L in lens) + 4, max_seqs=len(lens),
                          max_pages_per_seq=max(math.ceil(L / 16) for L in lens) + 1,
                          num_sinks=w.num_sinks if S is None else S, num_recent=w.num_recent if R is None else R,
-                         hadamard_block=block or w.hadamard_block, format=FORMATS[fmt])
+                         hadamard_block=block or w.hadamard_block, format=FORMATS[fmt], eviction=evict)
         cache = kv4.Cache(cfg, device)
         cache.append(list(range(len(lens))), lens, torch.cat([k for k, _ in kvs]).contiguous(),
                      torch.cat([v for _, v in kvs]).contiguous())

@@ -50,6 +50,13 @@ typedef enum kv4_format {
     KV4_FORMAT_BF16 = 2       /* raw bf16 pages, no rotation, no quantization (baseline) */
 } kv4_format;
 
+/* How a position that leaves the recent window reaches its INT4 copy (INT4_PROT only). */
+typedef enum kv4_eviction {
+    KV4_EVICT_DUAL_WRITE = 0, /* INT4 code quantized from the rotated values at append ([TOP5]) */
+    KV4_EVICT_REQUANT = 1     /* INT4 code re-quantized from the INT8 copy ([KV4]: tokens leaving the
+                                 window move from INT8 to INT4); see kv4_append */
+} kv4_eviction;
+
 typedef struct kv4_config {
     int32_t num_q_heads;       /* Hq; Hq % Hkv == 0 and G = Hq / Hkv in {1, 2, 4} */
     int32_t num_kv_heads;      /* Hkv >= 1 */
@@ -62,6 +69,7 @@ typedef struct kv4_config {
     int32_t num_recent;        /* R >= 0 INT8-protected trailing positions (INT4_PROT only) */
     int32_t hadamard_block;    /* b: power of two dividing D; 1 = no rotation ("plain INT4") */
     int32_t format;            /* kv4_format */
+    int32_t eviction;          /* kv4_eviction; must be KV4_EVICT_DUAL_WRITE for INT8 / BF16 */
 } kv4_config;
 
 /*
@@ -111,7 +119,8 @@ typedef struct kv4_buffers {
 typedef struct kv4_cache* kv4_cache_t;
 
 /* Sizes of the caller-allocated device buffers for `cfg`.  Errors: INVALID_ARGUMENT for a
- * malformed config (b not a power of two, D % b != 0, Hq % Hkv != 0, negative counts),
+ * malformed config (b not a power of two, D % b != 0, Hq % Hkv != 0, negative counts, an unknown
+ * eviction rule or KV4_EVICT_REQUANT outside INT4_PROT),
  * UNSUPPORTED for a valid config without a kernel (P != 16, D not in {64,128}, G not in {1,2,4}). */
 kv4_status kv4_buffer_sizes_query(const kv4_config* cfg, kv4_buffer_sizes* out);
 
@@ -142,7 +151,12 @@ kv4_status kv4_append_workspace_size(kv4_cache_t h, int32_t n_seqs, const int32_
  *   INT4 (Q = 15) is written to the page for every position; when t is in
  *   Prot(L) = {t < min(S, L)} u {max(S, L - R) <= t < L} the INT8 code (Q = 255, same y) is also
  *   written to the position's sink or ring slot.  A position that later leaves Prot is read from
- *   its INT4 page copy; nothing is re-quantized.  Zero results of z and s are stored as +0.
+ *   its INT4 page copy.  Zero results of z and s are stored as +0.
+ *   eviction = KV4_EVICT_DUAL_WRITE: the INT4 code is quantized from y (nothing is re-quantized).
+ *   eviction = KV4_EVICT_REQUANT: the INT4 code is quantized from the INT8 round trip
+ *   x8 = fl32(s8 * code8 + z8) of y (the move from INT8 to INT4 of a position leaving the window,
+ *   computed when the position is appended: x8 depends on the position alone, and doing it for
+ *   every position keeps a prefill equal to single appends).
  * INT8 format: Q = 255 in pages for every position.  BF16 format: bf16 rows copied.
  * Preconditions not checked per element: inputs finite, |y| <= 65504.
  * Errors: INVALID_ARGUMENT, OUT_OF_PAGES, SEQ_STATE (length would exceed max_pages_per_seq * P),

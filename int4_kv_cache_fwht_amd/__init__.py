@@ -14,6 +14,8 @@ from ._binding import (  # noqa: F401
     FORMAT_INT4_PROT,
     FORMAT_INT8,
     FORMAT_BF16,
+    EVICT_DUAL_WRITE,
+    EVICT_REQUANT,
     STATUS,
     lib,
     lib_path,
@@ -22,5 +24,5 @@ from ._binding import (  # noqa: F401
 
 lib()  # load now: a missing library fails the import, never a silent fallback
 
-__all__ = ["KV4Error", "Config", "BufferSizes", "Cache", "FORMAT_INT4_PROT", "FORMAT_INT8", "FORMAT_BF16", "STATUS",
-           "lib", "lib_path", "kv4_buffer_sizes_query"]
+__all__ = ["KV4Error", "Config", "BufferSizes", "Cache", "FORMAT_INT4_PROT", "FORMAT_INT8", "FORMAT_BF16",
+           "EVICT_DUAL_WRITE", "EVICT_REQUANT", "STATUS", "lib", "lib_path", "kv4_buffer_sizes_query"]

@@ -15,6 +15,9 @@ FORMAT_INT4_PROT = 0
 FORMAT_INT8 = 1
 FORMAT_BF16 = 2
 
+EVICT_DUAL_WRITE = 0
+EVICT_REQUANT = 1
+
 STATUS = {
     0: "KV4_OK",
     1: "KV4_ERR_INVALID_ARGUMENT",
@@ -36,7 +39,7 @@ class KV4Error(RuntimeError):
 class _Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_q_heads", "num_kv_heads", "head_dim", "page_size", "num_pages", "max_seqs", "max_pages_per_seq",
-        "num_sinks", "num_recent", "hadamard_block", "format")]
+        "num_sinks", "num_recent", "hadamard_block", "format", "eviction")]
 
 
 class _BufferSizes(ctypes.Structure):
@@ -68,6 +71,7 @@ class Config:
     hadamard_block: int = 128
     format: int = FORMAT_INT4_PROT
     page_size: int = 16
+    eviction: int = 0  # EVICT_DUAL_WRITE or EVICT_REQUANT
 
     def to_c(self) -> _Config:
         c = _Config()

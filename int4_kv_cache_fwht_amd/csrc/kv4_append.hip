@@ -161,7 +161,42 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a)
 
         const bool prot = (FMT == FMT_INT4_PROT) && active && is_protected(t, tk.len_new, a.sinks, a.recent);
 
+        // ---- INT8 codes: protected positions (INT4_PROT), every position (INT8 format), and every
+        // position when the INT4 codes are re-quantized from the INT8 round trip ----
+        const bool want8 = (FMT == FMT_INT8) ? active : prot;
+        const bool requant = (FMT == FMT_INT4_PROT) && a.requant != 0;
+        QuantParams qp8 = {};
+        uint32_t cb8[N / 4];
+        if (requant || __ballot(want8) != 0ull) {
+            qp8 = quant_params(mn, mx, 255.0f);
+#pragma unroll
+            for (int q = 0; q < N / 4; q++) {
+                uint32_t w = 0;
+                w = __builtin_amdgcn_cvt_pk_u8_f32((y[4 * q + 0] - qp8.zf) * qp8.inv, 0, w);
+                w = __builtin_amdgcn_cvt_pk_u8_f32((y[4 * q + 1] - qp8.zf) * qp8.inv, 1, w);
+                w = __builtin_amdgcn_cvt_pk_u8_f32((y[4 * q + 2] - qp8.zf) * qp8.inv, 2, w);
+                w = __builtin_amdgcn_cvt_pk_u8_f32((y[4 * q + 3] - qp8.zf) * qp8.inv, 3, w);
+                cb8[q] = w;
+            }
+        }
+
         if constexpr (FMT == FMT_INT4_PROT) {
+            if (requant) {
+                // the INT4 copy quantizes the INT8 round trip x8 = fl32(s8 * code8 + z8) (the
+                // product is exact, so the fma rounds once, like product-then-sum)
+                const float s8 = f16_bits_to_float(qp8.s_bits);
+#pragma unroll
+                for (int i = 0; i < N; i++) y[i] = fmaf(s8, (float)((cb8[i / 4] >> (8 * (i % 4))) & 0xFFu), qp8.zf);
+                mn = y[0];
+                mx = y[0];
+#pragma unroll
+                for (int i = 1; i < N; i++) {
+                    mn = fminf(mn, y[i]);
+                    mx = fmaxf(mx, y[i]);
+                }
+                mn = fminf(mn, dpp_xor1(mn));
+                mx = fmaxf(mx, dpp_xor1(mx));
+            }
             // ---- INT4 codes, natural nibble order: byte k = code[2k] | code[2k+1] << 4 ----
             const QuantParams qp = quant_params(mn, mx, 15.0f);
             uint32_t pk[N / 8];
@@ -200,20 +235,9 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a)
             }
         }
 
-        // ---- INT8 codes: protected positions (INT4_PROT) or every position (INT8 format) ----
-        const bool want8 = (FMT == FMT_INT8) ? active : prot;
-        if (__ballot(want8) != 0ull) {
-            const QuantParams qp = quant_params(mn, mx, 255.0f);
-            uint32_t cb8[N / 4];
-#pragma unroll
-            for (int q = 0; q < N / 4; q++) {
-                uint32_t w = 0;
-                w = __builtin_amdgcn_cvt_pk_u8_f32((y[4 * q + 0] - qp.zf) * qp.inv, 0, w);
-                w = __builtin_amdgcn_cvt_pk_u8_f32((y[4 * q + 1] - qp.zf) * qp.inv, 1, w);
-                w = __builtin_amdgcn_cvt_pk_u8_f32((y[4 * q + 2] - qp.zf) * qp.inv, 2, w);
-                w = __builtin_amdgcn_cvt_pk_u8_f32((y[4 * q + 3] - qp.zf) * qp.inv, 3, w);
-                cb8[q] = w;
-            }
+        // ---- INT8 stores ----
+        {
+            const QuantParams& qp = qp8;
             if (want8) {
                 uint8_t* tb;
                 int s8;
@@ -382,6 +406,35 @@ __global__ __launch_bounds__(64) void append_token_kernel(AppendArgs a)
         mx = fmaxf(mx, __shfl_xor(mx, m, 64));
     }
 
+    // ---- INT8 codes: protected position, or INT4 re-quantized from the INT8 round trip ----
+    const int t = tk.t0;
+    const bool prot = is_protected(t, tk.len_new, a.sinks, a.recent);
+    QuantParams qp8 = {};
+    uint32_t c8[PL];
+    if (prot || a.requant != 0) {
+        qp8 = quant_params(mn, mx, 255.0f);
+#pragma unroll
+        for (int i = 0; i < PL; i++) c8[i] = __builtin_amdgcn_cvt_pk_u8_f32((y[i] - qp8.zf) * qp8.inv, 0, 0u);
+    }
+    if (a.requant != 0) {
+        // x8 = fl32(s8 * code8 + z8): the product is exact, so the fma rounds once
+        const float s8f = f16_bits_to_float(qp8.s_bits);
+#pragma unroll
+        for (int i = 0; i < PL; i++) y[i] = fmaf(s8f, (float)c8[i], qp8.zf);
+        mn = y[0];
+        mx = y[0];
+#pragma unroll
+        for (int i = 1; i < PL; i++) {
+            mn = fminf(mn, y[i]);
+            mx = fmaxf(mx, y[i]);
+        }
+#pragma unroll
+        for (int m = 1; m < 32; m <<= 1) {
+            mn = fminf(mn, __shfl_xor(mn, m, 64));
+            mx = fmaxf(mx, __shfl_xor(mx, m, 64));
+        }
+    }
+
     // ---- INT4 page copy ----
     {
         const QuantParams qp = quant_params(mn, mx, 15.0f);
@@ -405,15 +458,12 @@ __global__ __launch_bounds__(64) void append_token_kernel(AppendArgs a)
     }
 
     // ---- INT8 copy when the position is protected ----
-    const int t = tk.t0;
-    if (is_protected(t, tk.len_new, a.sinks, a.recent)) {
-        const QuantParams qp = quant_params(mn, mx, 255.0f);
+    if (prot) {
+        const QuantParams& qp = qp8;
         const int u = (t < a.sinks) ? t : a.sinks + t % a.recent;
         uint8_t* tb = a.int8_pool + (((int64_t)tk.seq * a.hkv + h) * a.int8_tiles + (u >> 4)) * a.int8_tile;
         const int s8 = u & 15;
-        uint32_t c[PL];
-#pragma unroll
-        for (int i = 0; i < PL; i++) c[i] = __builtin_amdgcn_cvt_pk_u8_f32((y[i] - qp.zf) * qp.inv, 0, 0u);
+        const uint32_t (&c)[PL] = c8;
         constexpr int BB = 16 * D + 128; // the tile's two blocks
         if (row == 0) {
             // K of dims half x = d0 / (D/2): [D/32 chunks][16 slots][16 B], one byte per dim

@@ -203,6 +203,7 @@ kv4::Config to_config(const kv4_config* c)
     k.recent = c->num_recent;
     k.block = c->hadamard_block;
     k.format = c->format;
+    k.eviction = c->eviction;
     return k;
 }
 
@@ -453,6 +454,7 @@ kv4_status kv4_append(kv4_cache_t h, int32_t n_seqs, const int32_t* seq_ids, con
     a.recent = h->st.cfg.recent;
     a.int8_tiles = h->sizes.int8_tiles;
     a.cb = h->cb;
+    a.requant = h->st.cfg.eviction;
     std::vector<hipEvent_t> ev;
     if (h->prof.on) {
         e = Profiler::make(2, &ev);

@@ -21,6 +21,7 @@ struct AppendArgs {
     int hkv, block, sinks, recent, int8_tiles;
     float cb; // fl32(1/sqrt(block))
     int max_pps;
+    int requant; // INT4 codes from the INT8 round trip (eviction by re-quantization)
     // single-position appends of up to kArgEntries sequences: task e writes position arg_t0[e] of
     // sequence arg_seq[e] from row e into page arg_page[e] & 0x7fffffff (bit 31: allocated by
     // this call).  n_arg == 0: the tasks come from `tasks`.

@@ -34,6 +34,7 @@ enum Format : int { FMT_INT4_PROT = 0, FMT_INT8 = 1, FMT_BF16 = 2 };
 struct Config {
     int hq = 0, hkv = 0, d = 0, page = 0, num_pages = 0, max_seqs = 0, max_pps = 0;
     int sinks = 0, recent = 0, block = 1, format = 0;
+    int eviction = 0; // 0: dual write, 1: INT4 re-quantized from the INT8 round trip
 };
 
 struct Sizes {
@@ -58,6 +59,9 @@ inline Status check_config(const Config& c, std::string* msg)
     if (!is_pow2(c.block)) return bad(INVALID_ARGUMENT, "hadamard_block must be a power of two");
     if (c.d % c.block) return bad(INVALID_ARGUMENT, "hadamard_block must divide head_dim");
     if (c.format < 0 || c.format > 2) return bad(INVALID_ARGUMENT, "unknown format");
+    if (c.eviction < 0 || c.eviction > 1) return bad(INVALID_ARGUMENT, "unknown eviction rule");
+    if (c.eviction == 1 && c.format != FMT_INT4_PROT)
+        return bad(INVALID_ARGUMENT, "re-quantizing eviction needs the INT4_PROT format");
     if (c.page != kPageSize) return bad(UNSUPPORTED, "page_size must be 16");
     if (c.d != 64 && c.d != 128) return bad(UNSUPPORTED, "head_dim must be 64 or 128");
     int g = c.hq / c.hkv;

@@ -14,11 +14,12 @@ TOL = 2e-3  # max-abs error of decode outputs against the fp64 oracle on the sam
 
 class Pair:
     def __init__(self, hq, hkv, d, num_pages, max_seqs, max_pps, S=4, R=128, b=128, fmt=kv4.FORMAT_INT4_PROT,
-                 device="cuda"):
+                 device="cuda", eviction=kv4.EVICT_DUAL_WRITE):
         self.cfg = kv4.Config(num_q_heads=hq, num_kv_heads=hkv, head_dim=d, num_pages=num_pages, max_seqs=max_seqs,
-                              max_pages_per_seq=max_pps, num_sinks=S, num_recent=R, hadamard_block=b, format=fmt)
+                              max_pages_per_seq=max_pps, num_sinks=S, num_recent=R, hadamard_block=b, format=fmt,
+                              eviction=eviction)
         self.gpu = kv4.Cache(self.cfg, device)
-        self.ora = oracle.OracleCache(hq, hkv, d, 16, num_pages, max_seqs, max_pps, S, R, b, fmt)
+        self.ora = oracle.OracleCache(hq, hkv, d, 16, num_pages, max_seqs, max_pps, S, R, b, fmt, eviction=eviction)
         self.hq, self.hkv, self.d, self.S, self.R, self.b, self.fmt = hq, hkv, d, S, R, b, fmt
 
     def append(self, seq_ids, n_new, k, v):

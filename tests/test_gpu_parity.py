@@ -83,3 +83,30 @@ def test_group_and_dims(hq, hkv, d):
     err = np.abs(out - ref).max()
     print("gqa", hq, hkv, d, "max-abs", err)
     assert err <= TOL
+
+
+@pytest.mark.parametrize("S,R,b", [(4, 128, 128), (4, 32, 32), (0, 16, 1), (4, 0, 128)])
+def test_requant_eviction(S, R, b):
+    """INT4 codes re-quantized from the INT8 round trip: bit-exact pages, scales and INT8 slots after a
+    ragged prefill, single-position appends (the per-position kernel) and a second prefill; decode and
+    multi-query outputs within tolerance."""
+    _print_case("requant", S=S, R=R, b=b)
+    hq, hkv, d = 32, 8, 128
+    lens = [1, 17, 100, 132, 133, 300, 1000]
+    p = Pair(hq, hkv, d, num_pages=2048, max_seqs=16, max_pps=128, S=S, R=R, b=b, eviction=kv4.EVICT_REQUANT)
+    ks, vs = zip(*[_kv(L, hkv, d, seed=13, idx=i) for i, L in enumerate(lens)])
+    p.append(list(range(len(lens))), lens, torch.cat(ks).contiguous(), torch.cat(vs).contiguous())
+    for step in range(3):
+        kn, vn = _kv(len(lens), hkv, d, seed=15, idx=100 + step)
+        p.append(list(range(len(lens))), [1] * len(lens), kn, vn)
+    kb, vb = _kv(77, hkv, d, seed=17, idx=7)
+    p.append([9], [77], kb, vb)
+    assert p.compare_cache(list(range(len(lens))) + [9]) > 0
+    ids = list(range(len(lens))) + [9]
+    q = W.queries(len(ids), hq, d, 19, device="cuda")
+    out, ref = p.decode(ids, q)
+    assert np.abs(out - ref).max() <= TOL
+    nqs = [1, 3, 16, 20, 60, 64, 100, 77]
+    qm = W.queries(sum(nqs), hq, d, 21, device="cuda")
+    out, ref = p.multi(ids, nqs, qm)
+    assert np.abs(out - ref).max() <= TOL

@@ -97,7 +97,8 @@ def test_buffer_sizes_follow_documented_layout(libkv4, hq, hkv, d, S, R, b, fmt)
 @pytest.mark.parametrize("change,status", [
     (dict(head_dim=96, hadamard_block=32), 5), (dict(page_size=32), 5), (dict(num_q_heads=12, num_kv_heads=8), 1),
     (dict(num_q_heads=64, num_kv_heads=8), 5), (dict(hadamard_block=48), 1), (dict(hadamard_block=256), 1),
-    (dict(format=3), 1), (dict(num_sinks=-1), 1), (dict(max_seqs=0), 1), (dict(num_kv_heads=0), 1)])
+    (dict(format=3), 1), (dict(num_sinks=-1), 1), (dict(max_seqs=0), 1), (dict(num_kv_heads=0), 1),
+    (dict(eviction=2), 1), (dict(eviction=-1), 1), (dict(eviction=1, format=1), 1), (dict(eviction=1, format=2), 1)])
 def test_invalid_configs_are_rejected(libkv4, change, status):
     base = dict(num_q_heads=32, num_kv_heads=8, head_dim=128, num_pages=64, max_seqs=4, max_pages_per_seq=16,
                 num_sinks=4, num_recent=128, hadamard_block=128, format=0)
