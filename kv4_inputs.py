@@ -123,6 +123,15 @@ def bf16_bits(t: torch.Tensor) -> np.ndarray:
     return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
+def rope_tables(positions: int, head_dim: int, base: float = 1.0e6):
+    """Standard rotary-embedding tables (the caller's data for the fused RoPE append): float32
+    cos / sin [positions, head_dim / 2] of angle t * base^(-2i / head_dim), computed in float64.
+    base 1e6 is Qwen3's."""
+    inv = base ** (-np.arange(0, head_dim, 2, dtype=np.float64) / head_dim)
+    ang = np.arange(positions, dtype=np.float64)[:, None] * inv[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
 def tiny_inputs(device="cpu"):
     """The tiny workload: (K, V [300, 1, 64], q [1, 2, 64]) with seed 0."""
     w = WORKLOADS["tiny"]

@@ -104,6 +104,10 @@ def lib():
         L.kv4o_dequant_seq.restype = c_int
         L.kv4o_decode.argtypes = [P, c_int, P, P, c_double, P, c_int, P]
         L.kv4o_decode.restype = c_int
+        L.kv4o_rope_bf16.argtypes = [P, c_int, P, P, P]
+        L.kv4o_rope_bf16.restype = None
+        L.kv4o_append_rope.argtypes = [P, c_int, P, P, P, P, P, P, c_int]
+        L.kv4o_append_rope.restype = c_int
         L.kv4o_set_eviction.argtypes = [P, c_int]
         L.kv4o_set_eviction.restype = c_int
         L.kv4o_attend_multi.argtypes = [P, c_int, P, P, P, c_double, P, c_int, P]
@@ -170,6 +174,17 @@ def rotate_bf16(x_bits: np.ndarray, b: int) -> np.ndarray:
         lib().kv4o_rotate_bf16(_ptr(row), n, int(b), _ptr(o))
         out[r] = o
     return out.reshape(x_bits.shape)
+
+
+def rope_bf16(x_bits: np.ndarray, cos_row: np.ndarray, sin_row: np.ndarray) -> np.ndarray:
+    """RoPE (rotate-half pairs) of one bf16 row with one position's table rows -> float32 row."""
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    c = np.ascontiguousarray(cos_row, dtype=np.float32)
+    s = np.ascontiguousarray(sin_row, dtype=np.float32)
+    assert c.shape == s.shape == (x_bits.shape[0] // 2,)
+    out = np.empty(x_bits.shape[0], dtype=np.float32)
+    lib().kv4o_rope_bf16(_ptr(x_bits), x_bits.shape[0], _ptr(c), _ptr(s), _ptr(out))
+    return out
 
 
 def quantize(y: np.ndarray, Q: int) -> Tuple[np.ndarray, int, int]:
@@ -262,6 +277,20 @@ class OracleCache:
             assert k_bits.shape == (int(nn.sum()), self.hkv, self.d) and v_bits.shape == k_bits.shape
             kp, vp = _ptr(k_bits), _ptr(v_bits)
         return lib().kv4o_append(self._h, ids.shape[0], _ptr(ids), _ptr(nn), kp, vp)
+
+    def append_rope(self, seq_ids: Sequence[int], n_new: Sequence[int], k_bits: np.ndarray, v_bits: np.ndarray,
+                    rope_cos: np.ndarray, rope_sin: np.ndarray) -> int:
+        """Like append with pre-RoPE keys; rope_cos / rope_sin: float32 [positions, d/2]."""
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int32)
+        nn = np.ascontiguousarray(n_new, dtype=np.int32)
+        k_bits = np.ascontiguousarray(k_bits, dtype=np.uint16)
+        v_bits = np.ascontiguousarray(v_bits, dtype=np.uint16)
+        assert k_bits.shape == (int(nn.sum()), self.hkv, self.d) and v_bits.shape == k_bits.shape
+        c = np.ascontiguousarray(rope_cos, dtype=np.float32)
+        s = np.ascontiguousarray(rope_sin, dtype=np.float32)
+        assert c.shape == s.shape and c.shape[1] == self.d // 2
+        return lib().kv4o_append_rope(self._h, ids.shape[0], _ptr(ids), _ptr(nn), _ptr(k_bits), _ptr(v_bits), _ptr(c),
+                                      _ptr(s), c.shape[0])
 
     # -- contents ------------------------------------------------------------------------------
     def page_token(self, seq: int, t: int, h: int, kv: int):

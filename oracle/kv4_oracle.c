@@ -190,6 +190,23 @@ void kv4o_fwht_f32(float* y, int n, int b)
     }
 }
 
+/* Rotary position embedding of one bf16 key row at one position, rotate-half pairing: for
+ * i < n/2 the pair (x_i, x_{i+n/2}) with c = cos_row[i], s = sin_row[i] becomes
+ *   (fl32(fl32(x_i c) - fl32(x_{i+n/2} s)),  fl32(fl32(x_{i+n/2} c) + fl32(x_i s))).
+ * The tables are the caller's (the pages apply the Hadamard transform to keys after RoPE and
+ * leave RoPE itself to the model). */
+void kv4o_rope_bf16(const uint16_t* x, int n, const float* cos_row, const float* sin_row, float* out)
+{
+    int half = n / 2;
+    for (int i = 0; i < half; i++) {
+        float a = bf16_to_float(x[i]), b = bf16_to_float(x[i + half]);
+        float c = cos_row[i], s = sin_row[i];
+        float ac = a * c, bs = b * s, bc = b * c, as = a * s;
+        out[i] = ac - bs;
+        out[i + half] = bc + as;
+    }
+}
+
 /* bf16 row -> rotated binary32 row. */
 void kv4o_rotate_bf16(const uint16_t* x, int n, int b, float* y)
 {
@@ -472,8 +489,11 @@ int kv4o_seq_free(kv4o_cache* c, int seq)
 }
 
 /* Writes one token (all heads, K and V) at position t of seq; L_new is the length after the
- * call, which decides INT8 protection.  k, v: [hkv][d] bf16 bits, or NULL (allocation only). */
-static int write_token(kv4o_cache* c, int seq, int t, int L_new, const uint16_t* k, const uint16_t* v)
+ * call, which decides INT8 protection.  k, v: [hkv][d] bf16 bits, or NULL (allocation only).
+ * rope_cos / rope_sin: NULL, or this position's table rows [d/2]: the key rows then get RoPE
+ * (kv4o_rope_bf16) before the Hadamard rotation. */
+static int write_token(kv4o_cache* c, int seq, int t, int L_new, const uint16_t* k, const uint16_t* v,
+                       const float* rope_cos, const float* rope_sin)
 {
     int page = c->bt[(size_t)seq * c->max_pps + t / c->P];
     int slot = t % c->P;
@@ -496,7 +516,12 @@ static int write_token(kv4o_cache* c, int seq, int t, int L_new, const uint16_t*
                 memcpy(c->bf + pi * c->d, x, (size_t)c->d * sizeof(uint16_t));
                 continue;
             }
-            kv4o_rotate_bf16(x, c->d, c->b, y);
+            if (kv == 0 && rope_cos) {
+                kv4o_rope_bf16(x, c->d, rope_cos, rope_sin, y);
+                kv4o_fwht_f32(y, c->d, c->b);
+            } else {
+                kv4o_rotate_bf16(x, c->d, c->b, y);
+            }
             int Q = (c->fmt == KV4O_FMT_INT8) ? 255 : 15;
             if (c->requant) {
                 /* INT4 from the INT8 round trip: x8 = fl32(s8 * code8 + z8) (the product is exact) */
@@ -536,11 +561,32 @@ static int write_token(kv4o_cache* c, int seq, int t, int L_new, const uint16_t*
     return rc;
 }
 
+static int append_rows(kv4o_cache* c, int n_seqs, const int* seq_ids, const int* n_new, const uint16_t* k_new,
+                       const uint16_t* v_new, const float* rope_cos, const float* rope_sin, int rope_positions);
+
 /* Appends n_new[i] tokens to seq_ids[i], for i in call order.  Rows of k_new / v_new are ordered
  * by (call order, ascending position), each row [hkv][d] bf16.  All-or-nothing on page
  * shortage: if the free list cannot cover every new page of the call, nothing changes. */
 int kv4o_append(kv4o_cache* c, int n_seqs, const int* seq_ids, const int* n_new, const uint16_t* k_new,
                 const uint16_t* v_new)
+{
+    return append_rows(c, n_seqs, seq_ids, n_new, k_new, v_new, NULL, NULL, 0);
+}
+
+/* The same with pre-RoPE keys: the key row of position t gets RoPE with table rows
+ * rope_cos[t], rope_sin[t] ([rope_positions][d/2] binary32) before the Hadamard rotation.  Every
+ * new position must be < rope_positions.  The RoPE output is not rounded to bf16: the cache
+ * stores the rotation of the binary32 RoPE output. */
+int kv4o_append_rope(kv4o_cache* c, int n_seqs, const int* seq_ids, const int* n_new, const uint16_t* k_new,
+                     const uint16_t* v_new, const float* rope_cos, const float* rope_sin, int rope_positions)
+{
+    if (!rope_cos || !rope_sin || rope_positions < 0)
+        return KV4O_INVALID_ARGUMENT;
+    return append_rows(c, n_seqs, seq_ids, n_new, k_new, v_new, rope_cos, rope_sin, rope_positions);
+}
+
+static int append_rows(kv4o_cache* c, int n_seqs, const int* seq_ids, const int* n_new, const uint16_t* k_new,
+                       const uint16_t* v_new, const float* rope_cos, const float* rope_sin, int rope_positions)
 {
     if (n_seqs < 0)
         return KV4O_INVALID_ARGUMENT;
@@ -555,6 +601,8 @@ int kv4o_append(kv4o_cache* c, int n_seqs, const int* seq_ids, const int* n_new,
         long L0 = c->len[s], L1 = L0 + n_new[i];
         if (L1 > (long)c->max_pps * c->P)
             return KV4O_SEQ_STATE;
+        if (rope_cos && L1 > rope_positions)
+            return KV4O_INVALID_ARGUMENT;
         needed += (L1 + c->P - 1) / c->P - (L0 + c->P - 1) / c->P;
     }
     if (needed > c->fifo_count)
@@ -567,8 +615,10 @@ int kv4o_append(kv4o_cache* c, int n_seqs, const int* seq_ids, const int* n_new,
         for (int t = L0; t < L1; t++, row++) {
             if (t % c->P == 0)
                 c->bt[(size_t)s * c->max_pps + t / c->P] = fifo_pop(c);
+            size_t half = (size_t)c->d / 2;
             int rc = write_token(c, s, t, L1, k_new ? k_new + row * row_elems : NULL,
-                                 v_new ? v_new + row * row_elems : NULL);
+                                 v_new ? v_new + row * row_elems : NULL, rope_cos ? rope_cos + (size_t)t * half : NULL,
+                                 rope_sin ? rope_sin + (size_t)t * half : NULL);
             if (rc != KV4O_OK)
                 return rc;
         }
