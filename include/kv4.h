@@ -166,6 +166,21 @@ kv4_status kv4_append(kv4_cache_t h, int32_t n_seqs, const int32_t* seq_ids, con
                       const void* k_new, const void* v_new, void* workspace, size_t ws_bytes,
                       void* stream /* hipStream_t; NULL = null stream */);
 
+/*
+ * kv4_append with keys given before RoPE: the append applies RoPE to each key row and then
+ * everything kv4_append does (the pages apply the Hadamard transform to keys after RoPE; this
+ * fuses the two so the post-RoPE keys never go to memory).  For position t and i < D/2, with
+ * c = rope_cos[t][i], s = rope_sin[t][i] (binary32, caller-owned device tables [rope_positions][D/2]):
+ *   (x_i, x_{i+D/2}) -> (fl32(fl32(x_i c) - fl32(x_{i+D/2} s)), fl32(fl32(x_{i+D/2} c) + fl32(x_i s)))
+ * (rotate-half pairing).  The binary32 result is rotated and quantized as is (no bf16 rounding in
+ * between).  Values are unchanged.  Every new position must be < rope_positions.
+ * Formats: INT4_PROT and INT8 (BF16: UNSUPPORTED).  Other errors as kv4_append.
+ */
+kv4_status kv4_append_rope(kv4_cache_t h, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_new,
+                           const void* k_new, const void* v_new, const float* rope_cos, const float* rope_sin,
+                           int32_t rope_positions, void* workspace, size_t ws_bytes,
+                           void* stream /* hipStream_t */);
+
 /* Releases a sequence: length -> 0, its pages go to the back of the free list in block-table
  * order.  Host state only.  Error: INVALID_ARGUMENT for a bad id. */
 kv4_status kv4_seq_free(kv4_cache_t h, int32_t seq_id);
@@ -211,6 +226,13 @@ kv4_status kv4_multi_query_workspace_size(kv4_cache_t h, int32_t n_seqs, const i
  */
 kv4_status kv4_multi_query_attention(kv4_cache_t h, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_q,
                                      const void* q, float scale, float* out, void* workspace, size_t ws_bytes,
+                                     void* stream /* hipStream_t */);
+
+/* kv4_decode_attention with bf16 output: out (device) bf16 [n_seqs][Hq][D], each value the
+ * round-to-nearest-even of the fp32 result kv4_decode_attention returns for the same call (for
+ * the next layer of a model that runs in bf16).  Same arguments, workspace and errors. */
+kv4_status kv4_decode_attention_bf16(kv4_cache_t h, int32_t n_seqs, const int32_t* seq_ids, const void* q,
+                                     float scale, void* out, void* workspace, size_t ws_bytes,
                                      void* stream /* hipStream_t */);
 
 /* Host-state queries. */

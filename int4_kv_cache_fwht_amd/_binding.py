@@ -111,9 +111,11 @@ def lib():
         L.kv4_cache_destroy.argtypes = [P]
         L.kv4_append_workspace_size.argtypes = [P, I32, P, P, P]
         L.kv4_append.argtypes = [P, I32, P, P, P, P, P, SZ, P]
+        L.kv4_append_rope.argtypes = [P, I32, P, P, P, P, P, P, I32, P, SZ, P]
         L.kv4_seq_free.argtypes = [P, I32]
         L.kv4_decode_workspace_size.argtypes = [P, I32, P]
         L.kv4_decode_attention.argtypes = [P, I32, P, P, ctypes.c_float, P, P, SZ, P]
+        L.kv4_decode_attention_bf16.argtypes = [P, I32, P, P, ctypes.c_float, P, P, SZ, P]
         L.kv4_multi_query_workspace_size.argtypes = [P, I32, P, P, P]
         L.kv4_multi_query_attention.argtypes = [P, I32, P, P, P, ctypes.c_float, P, P, SZ, P]
         L.kv4_seq_length.argtypes = [P, I32, P]
@@ -127,7 +129,7 @@ def lib():
         L.kv4_last_error.argtypes = [P]
         L.kv4_last_error.restype = ctypes.c_char_p
         for name in ("kv4_buffer_sizes_query", "kv4_cache_create", "kv4_cache_destroy", "kv4_append_workspace_size",
-                     "kv4_append", "kv4_seq_free", "kv4_decode_workspace_size", "kv4_decode_attention",
+                     "kv4_append", "kv4_append_rope", "kv4_seq_free", "kv4_decode_workspace_size", "kv4_decode_attention", "kv4_decode_attention_bf16",
                      "kv4_multi_query_workspace_size", "kv4_multi_query_attention",
                      "kv4_seq_length", "kv4_block_table", "kv4_free_pages", "kv4_set_decode_waves",
                      "kv4_profile_enable", "kv4_profile_read"):
@@ -246,6 +248,30 @@ class Cache:
         _check(lib().kv4_append(self._h, len(ids), ids, nn, kp, vp, workspace.data_ptr(), workspace.numel(), st),
                self._h)
 
+    def append_rope(self, seq_ids: Sequence[int], n_new: Sequence[int], k: torch.Tensor, v: torch.Tensor,
+                    rope_cos: torch.Tensor, rope_sin: torch.Tensor, stream=None,
+                    workspace: Optional[torch.Tensor] = None):
+        """Append with pre-RoPE keys; rope_cos / rope_sin: float32 [positions, D/2] on the device."""
+        ids, nn = _i32_array(seq_ids), _i32_array(n_new)
+        rows = sum(int(x) for x in n_new)
+        for t in (k, v):
+            if t.dtype != torch.bfloat16 or not t.is_contiguous() or t.device != self.device:
+                raise ValueError("k / v must be contiguous bf16 tensors on the cache device")
+            if tuple(t.shape) != (rows, self.cfg.num_kv_heads, self.cfg.head_dim):
+                raise ValueError("k / v shape must be [sum(n_new), Hkv, D]")
+        for t in (rope_cos, rope_sin):
+            if t.dtype != torch.float32 or not t.is_contiguous() or t.device != self.device or t.dim() != 2 \
+                    or t.shape[1] != self.cfg.head_dim // 2:
+                raise ValueError("RoPE tables must be contiguous float32 [positions, D/2] on the cache device")
+        if rope_cos.shape != rope_sin.shape:
+            raise ValueError("RoPE tables differ in shape")
+        if workspace is None:
+            workspace = self._workspace("_ws_append", self.append_workspace_size(seq_ids, n_new))
+        st = _stream_ptr(stream)
+        _check(lib().kv4_append_rope(self._h, len(ids), ids, nn, k.data_ptr(), v.data_ptr(), rope_cos.data_ptr(),
+                                     rope_sin.data_ptr(), rope_cos.shape[0], workspace.data_ptr(), workspace.numel(),
+                                     st), self._h)
+
     def decode_attention(self, seq_ids: Sequence[int], q: torch.Tensor, scale: float = 0.0,
                          out: Optional[torch.Tensor] = None, stream=None,
                          workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
@@ -289,6 +315,26 @@ class Cache:
             workspace = self._workspace("_ws_mq", self.multi_query_workspace_size(seq_ids, n_q))
         st = _stream_ptr(stream)
         _check(lib().kv4_multi_query_attention(self._h, len(ids), ids, nq, q.data_ptr(), float(scale), out.data_ptr(),
+                                               workspace.data_ptr(), workspace.numel(), st), self._h)
+        return out
+
+    def decode_attention_bf16(self, seq_ids: Sequence[int], q: torch.Tensor, scale: float = 0.0,
+                              out: Optional[torch.Tensor] = None, stream=None,
+                              workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """q: bf16 [n, Hq, D] -> bf16 [n, Hq, D] (the fp32 result rounded to nearest even)."""
+        ids = _i32_array(seq_ids)
+        n = len(ids)
+        shape = (n, self.cfg.num_q_heads, self.cfg.head_dim)
+        if q.dtype != torch.bfloat16 or not q.is_contiguous() or tuple(q.shape) != shape or q.device != self.device:
+            raise ValueError("q must be a contiguous bf16 [n, Hq, D] tensor on the cache device")
+        if out is None:
+            out = torch.empty(shape, dtype=torch.bfloat16, device=self.device)
+        elif out.dtype != torch.bfloat16 or not out.is_contiguous() or tuple(out.shape) != shape:
+            raise ValueError("out must be a contiguous bf16 [n, Hq, D] tensor")
+        if workspace is None:
+            workspace = self._workspace("_ws_decode", self.decode_workspace_size(n))
+        st = _stream_ptr(stream)
+        _check(lib().kv4_decode_attention_bf16(self._h, n, ids, q.data_ptr(), float(scale), out.data_ptr(),
                                                workspace.data_ptr(), workspace.numel(), st), self._h)
         return out
 

@@ -143,6 +143,25 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a)
                 y[8 * q + 2 * j + 1] = as_float(raw[q][j] & 0xFFFF0000u);
             }
         }
+        // ---- fused RoPE of key rows: the pair (i, i + D/2) is element i of the row's two halves;
+        // binary32, (x_i c - x_{i+D/2} s, x_{i+D/2} c + x_i s) with the caller's table row of t ----
+        if (a.rope_cos != nullptr && !is_v) {
+            const int tr = active ? t : 0;
+            const float* cr = a.rope_cos + (int64_t)tr * N;
+            const float* sr = a.rope_sin + (int64_t)tr * N;
+#pragma unroll
+            for (int q = 0; q < N / 4; q++) {
+                const float4_t c4 = *(const float4_t*)(cr + 4 * q);
+                const float4_t s4 = *(const float4_t*)(sr + 4 * q);
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const float own = y[4 * q + j];
+                    const float other = dpp_xor1(own);
+                    const float oc = own * c4[j], os = other * s4[j];
+                    y[4 * q + j] = half ? oc + os : oc - os;
+                }
+            }
+        }
         fwht_in_lane<N>(y, a.block);
         if (a.block == D) fwht_across_pair<N>(y, half);
         if (a.block > 1) {
@@ -367,6 +386,19 @@ __global__ __launch_bounds__(64) void append_token_kernel(AppendArgs a)
     float y[PL];
 #pragma unroll
     for (int j = 0; j < PL; j++) y[j] = as_float((uint32_t)raw[j] << 16);
+    // fused RoPE of the key row: lanes l and l ^ 16 hold the pairs (i, i + D/2)
+    if (a.rope_cos != nullptr) {
+        const float* cr = a.rope_cos + (int64_t)tk.t0 * (D / 2) + PL * (l32 & 15);
+        const float* sr = a.rope_sin + (int64_t)tk.t0 * (D / 2) + PL * (l32 & 15);
+#pragma unroll
+        for (int j = 0; j < PL; j++) {
+            const float own = y[j];
+            const float other = __shfl_xor(own, 16, 64);
+            const float oc = own * cr[j], os = other * sr[j];
+            const float r = (l32 & 16) ? oc + os : oc - os;
+            y[j] = row == 0 ? r : own;
+        }
+    }
     // stages h = 1, 2, ... < b in order
 #pragma unroll
     for (int hh = 1; hh < PL; hh <<= 1) {

@@ -900,7 +900,8 @@ __device__ __forceinline__ int64_t wave_of_step(int64_t step, int64_t T, int64_t
     return w < W - 1 ? w : W - 1;
 }
 
-template <int D, int G, int FMT>
+// OUT16: the output rows are bf16 (round to nearest even of the fp32 result) at a.out.
+template <int D, int G, int FMT, bool OUT16 = false>
 __global__ __launch_bounds__(64 * G) void merge_kernel(DecodeArgs a)
 {
     constexpr int NHV = D / 64;
@@ -963,9 +964,19 @@ __global__ __launch_bounds__(64 * G) void merge_kernel(DecodeArgs a)
 #pragma unroll
         for (int hv = 0; hv < NHV; hv++) r[hv] = r[hv] * a.cb;
     }
-    float* o = a.out + ((int64_t)U.entry * (a.hkv * G) + U.head * G + i) * D + lane;
+    const int64_t oi = ((int64_t)U.entry * (a.hkv * G) + U.head * G + i) * D + lane;
+    if constexpr (OUT16) {
+        uint16_t* o = (uint16_t*)a.out + oi;
 #pragma unroll
-    for (int hv = 0; hv < NHV; hv++) o[64 * hv] = r[hv];
+        for (int hv = 0; hv < NHV; hv++) {
+            const uint32_t x = as_uint(r[hv]);
+            o[64 * hv] = (uint16_t)((x + 0x7FFFu + ((x >> 16) & 1u)) >> 16);
+        }
+    } else {
+        float* o = a.out + oi;
+#pragma unroll
+        for (int hv = 0; hv < NHV; hv++) o[64 * hv] = r[hv];
+    }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -984,6 +995,13 @@ template <int D, int G, int F>
 static hipError_t launch_merge_t(const DecodeArgs& a, hipStream_t stream)
 {
     hipLaunchKernelGGL((merge_kernel<D, G, F>), dim3((unsigned)a.n_units), dim3(64 * G), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int D, int G, int F>
+static hipError_t launch_merge16_t(const DecodeArgs& a, hipStream_t stream)
+{
+    hipLaunchKernelGGL((merge_kernel<D, G, F, true>), dim3((unsigned)a.n_units), dim3(64 * G), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -1038,6 +1056,11 @@ hipError_t decode_split_residency(int d, int g, int format, int* blocks_per_cu)
 hipError_t launch_decode_merge(int d, int g, int format, const DecodeArgs& a, hipStream_t stream)
 {
     KV4_DEC_DISPATCH(launch_merge_t)
+}
+
+hipError_t launch_decode_merge_bf16(int d, int g, int format, const DecodeArgs& a, hipStream_t stream)
+{
+    KV4_DEC_DISPATCH(launch_merge16_t)
 }
 
 #undef KV4_DEC_DISPATCH

@@ -387,8 +387,14 @@ kv4_status kv4_append_workspace_size(kv4_cache_t h, int32_t n_seqs, const int32_
     return KV4_OK;
 }
 
-kv4_status kv4_append(kv4_cache_t h, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_new, const void* k_new,
-                      const void* v_new, void* workspace, size_t ws_bytes, void* stream)
+} // extern "C"
+
+namespace {
+
+// kv4_append and kv4_append_rope: rope_cos == nullptr is the plain append.
+kv4_status append_impl(kv4_cache_t h, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_new, const void* k_new,
+                       const void* v_new, void* workspace, size_t ws_bytes, void* stream, const float* rope_cos,
+                       const float* rope_sin, int32_t rope_positions)
 {
     if (!h) return fail(nullptr, KV4_ERR_INVALID_ARGUMENT, "null handle");
     if (n_seqs < 0 || (n_seqs > 0 && (!seq_ids || !n_new))) return fail(h, KV4_ERR_INVALID_ARGUMENT, "bad argument list");
@@ -396,6 +402,16 @@ kv4_status kv4_append(kv4_cache_t h, int32_t n_seqs, const int32_t* seq_ids, con
     for (int i = 0; i < n_seqs; i++) {
         if (n_new[i] < 0) return fail(h, KV4_ERR_INVALID_ARGUMENT, "n_new < 0");
         rows += n_new[i];
+    }
+    if (rope_cos) {
+        if (h->st.cfg.format == kv4::FMT_BF16)
+            return fail(h, KV4_ERR_UNSUPPORTED, "the fused RoPE append needs a quantized format");
+        if (!rope_sin || rope_positions < 0) return fail(h, KV4_ERR_INVALID_ARGUMENT, "bad RoPE tables");
+        for (int i = 0; i < n_seqs; i++) {
+            if (seq_ids[i] < 0 || seq_ids[i] >= h->st.cfg.max_seqs) continue; // the planner rejects it
+            if ((int64_t)h->st.len[(size_t)seq_ids[i]] + n_new[i] > rope_positions)
+                return fail(h, KV4_ERR_INVALID_ARGUMENT, "a new position is beyond the RoPE tables");
+        }
     }
     if (rows > 0 && (!k_new || !v_new)) return fail(h, KV4_ERR_INVALID_ARGUMENT, "null k_new / v_new");
     const size_t need = align_up(append_task_bound(n_seqs, n_new) * sizeof(kv4::AppendTask));
@@ -455,6 +471,8 @@ kv4_status kv4_append(kv4_cache_t h, int32_t n_seqs, const int32_t* seq_ids, con
     a.int8_tiles = h->sizes.int8_tiles;
     a.cb = h->cb;
     a.requant = h->st.cfg.eviction;
+    a.rope_cos = rope_cos;
+    a.rope_sin = rope_sin;
     std::vector<hipEvent_t> ev;
     if (h->prof.on) {
         e = Profiler::make(2, &ev);
@@ -474,6 +492,26 @@ kv4_status kv4_append(kv4_cache_t h, int32_t n_seqs, const int32_t* seq_ids, con
     return KV4_OK;
 }
 
+} // namespace
+
+extern "C" {
+
+kv4_status kv4_append(kv4_cache_t h, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_new, const void* k_new,
+                      const void* v_new, void* workspace, size_t ws_bytes, void* stream)
+{
+    return append_impl(h, n_seqs, seq_ids, n_new, k_new, v_new, workspace, ws_bytes, stream, nullptr, nullptr, 0);
+}
+
+kv4_status kv4_append_rope(kv4_cache_t h, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_new,
+                           const void* k_new, const void* v_new, const float* rope_cos, const float* rope_sin,
+                           int32_t rope_positions, void* workspace, size_t ws_bytes, void* stream)
+{
+    if (!h) return fail(nullptr, KV4_ERR_INVALID_ARGUMENT, "null handle");
+    if (!rope_cos || !rope_sin) return fail(h, KV4_ERR_INVALID_ARGUMENT, "null RoPE tables");
+    return append_impl(h, n_seqs, seq_ids, n_new, k_new, v_new, workspace, ws_bytes, stream, rope_cos, rope_sin,
+                       rope_positions);
+}
+
 kv4_status kv4_seq_free(kv4_cache_t h, int32_t seq_id)
 {
     if (!h) return fail(nullptr, KV4_ERR_INVALID_ARGUMENT, "null handle");
@@ -490,9 +528,14 @@ kv4_status kv4_decode_workspace_size(kv4_cache_t h, int32_t n_seqs, size_t* byte
     return KV4_OK;
 }
 
-kv4_status kv4_decode_attention(kv4_cache_t h, int32_t n_seqs, const int32_t* seq_ids, const void* q, float scale,
-                                float* out, void* workspace, size_t ws_bytes, void* stream)
+} // extern "C"
+
+namespace {
+
+kv4_status decode_impl(kv4_cache_t h, int32_t n_seqs, const int32_t* seq_ids, const void* q, float scale, void* out_ptr,
+                       bool out16, void* workspace, size_t ws_bytes, void* stream)
 {
+    float* out = (float*)out_ptr;
     if (!h) return fail(nullptr, KV4_ERR_INVALID_ARGUMENT, "null handle");
     if (n_seqs < 0 || (n_seqs > 0 && (!seq_ids || !q || !out))) return fail(h, KV4_ERR_INVALID_ARGUMENT, "bad argument list");
     if (!std::isfinite(scale)) return fail(h, KV4_ERR_INVALID_ARGUMENT, "scale must be finite");
@@ -577,7 +620,8 @@ kv4_status kv4_decode_attention(kv4_cache_t h, int32_t n_seqs, const int32_t* se
         e = hipEventRecord(ev[1], strm);
         if (e != hipSuccess) return hip_fail(h, e, "profiling event");
     }
-    e = kv4::launch_decode_merge(D, G, h->st.cfg.format, a, strm);
+    e = out16 ? kv4::launch_decode_merge_bf16(D, G, h->st.cfg.format, a, strm)
+              : kv4::launch_decode_merge(D, G, h->st.cfg.format, a, strm);
     if (e != hipSuccess) return hip_fail(h, e, "decode merge launch");
     if (h->prof.on) {
         e = hipEventRecord(ev[2], strm);
@@ -585,6 +629,22 @@ kv4_status kv4_decode_attention(kv4_cache_t h, int32_t n_seqs, const int32_t* se
         h->prof.decode_ev.push_back(ev);
     }
     return KV4_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+kv4_status kv4_decode_attention(kv4_cache_t h, int32_t n_seqs, const int32_t* seq_ids, const void* q, float scale,
+                                float* out, void* workspace, size_t ws_bytes, void* stream)
+{
+    return decode_impl(h, n_seqs, seq_ids, q, scale, out, false, workspace, ws_bytes, stream);
+}
+
+kv4_status kv4_decode_attention_bf16(kv4_cache_t h, int32_t n_seqs, const int32_t* seq_ids, const void* q,
+                                     float scale, void* out, void* workspace, size_t ws_bytes, void* stream)
+{
+    return decode_impl(h, n_seqs, seq_ids, q, scale, out, true, workspace, ws_bytes, stream);
 }
 
 kv4_status kv4_multi_query_workspace_size(kv4_cache_t h, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_q,

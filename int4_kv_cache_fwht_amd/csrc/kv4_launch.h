@@ -22,6 +22,9 @@ struct AppendArgs {
     float cb; // fl32(1/sqrt(block))
     int max_pps;
     int requant; // INT4 codes from the INT8 round trip (eviction by re-quantization)
+    // fused RoPE of the key rows (nullptr: keys are taken as given): float [position][D/2]
+    const float* rope_cos;
+    const float* rope_sin;
     // single-position appends of up to kArgEntries sequences: task e writes position arg_t0[e] of
     // sequence arg_seq[e] from row e into page arg_page[e] & 0x7fffffff (bit 31: allocated by
     // this call).  n_arg == 0: the tasks come from `tasks`.
@@ -78,6 +81,8 @@ hipError_t launch_append(int d, int format, int n_tasks, const AppendArgs& a, hi
 hipError_t launch_append_token(int d, int n_tasks, const AppendArgs& a, hipStream_t stream);
 hipError_t launch_decode_split(int d, int g, int format, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_merge(int d, int g, int format, const DecodeArgs& a, hipStream_t stream);
+// The same merge writing bf16 output rows (a.out then points at bf16 [entries][hq][D]).
+hipError_t launch_decode_merge_bf16(int d, int g, int format, const DecodeArgs& a, hipStream_t stream);
 // Workgroups of the split kernel (4 waves each) that fit on one compute unit at once.
 hipError_t decode_split_residency(int d, int g, int format, int* blocks_per_cu);
 // Multi-query attention (INT4_PROT and INT8 formats): split kernel over the call's wave tasks,

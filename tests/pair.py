@@ -30,6 +30,13 @@ class Pair:
         rc = self.ora.append(seq_ids, n_new, kb, vb)
         assert rc == oracle.OK, rc
 
+    def append_rope(self, seq_ids, n_new, k, v, cos, sin):
+        """cos, sin: float32 numpy tables [positions, d/2] (copied to the device for the GPU side)."""
+        self.gpu.append_rope(seq_ids, n_new, k, v, torch.from_numpy(cos).to(k.device),
+                             torch.from_numpy(sin).to(k.device))
+        rc = self.ora.append_rope(seq_ids, n_new, bf16_bits(k), bf16_bits(v), cos, sin)
+        assert rc == oracle.OK, rc
+
     def decode(self, seq_ids, q, scale=0.0):
         out = self.gpu.decode_attention(seq_ids, q, scale=scale)
         ref, _ = self.ora.decode(seq_ids, bf16_bits(q), scale=scale)

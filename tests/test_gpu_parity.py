@@ -110,3 +110,73 @@ def test_requant_eviction(S, R, b):
     qm = W.queries(sum(nqs), hq, d, 21, device="cuda")
     out, ref = p.multi(ids, nqs, qm)
     assert np.abs(out - ref).max() <= TOL
+
+
+@pytest.mark.parametrize("fmt,b,S,R", [
+    (kv4.FORMAT_INT4_PROT, 128, 4, 128),
+    (kv4.FORMAT_INT4_PROT, 32, 4, 32),
+    (kv4.FORMAT_INT8, 128, 0, 0),
+])
+def test_rope_append(fmt, b, S, R):
+    """Fused RoPE append (pre-RoPE keys, Qwen3-style tables): bit-exact pages, scales and INT8 slots
+    after a ragged prefill (page kernel), single-position appends (per-position kernel) and a second
+    prefill; decode within tolerance."""
+    _print_case("rope", fmt=fmt, b=b, S=S, R=R)
+    hq, hkv, d = 32, 8, 128
+    cos, sin = W.rope_tables(2048, d)
+    lens = [1, 17, 100, 132, 133, 300, 1000]
+    p = Pair(hq, hkv, d, num_pages=2048, max_seqs=16, max_pps=128, S=S, R=R, b=b, fmt=fmt)
+    ks, vs = zip(*[_kv(L, hkv, d, seed=23, idx=i) for i, L in enumerate(lens)])
+    p.append_rope(list(range(len(lens))), lens, torch.cat(ks).contiguous(), torch.cat(vs).contiguous(), cos, sin)
+    for step in range(3):
+        kn, vn = _kv(len(lens), hkv, d, seed=25, idx=100 + step)
+        p.append_rope(list(range(len(lens))), [1] * len(lens), kn, vn, cos, sin)
+    kb, vb = _kv(45, hkv, d, seed=27, idx=7)
+    p.append_rope([9], [45], kb, vb, cos, sin)
+    ids = list(range(len(lens))) + [9]
+    assert p.compare_cache(ids) > 0
+    out, ref = p.decode(ids, W.queries(len(ids), hq, d, 29, device="cuda"))
+    assert np.abs(out - ref).max() <= TOL
+
+
+def test_rope_append_errors():
+    _print_case("rope_errors")
+    hq, hkv, d = 8, 2, 64
+    cos, sin = W.rope_tables(40, d)
+    p = Pair(hq, hkv, d, num_pages=64, max_seqs=4, max_pps=8, S=4, R=16, b=64)
+    k, v = _kv(30, hkv, d, seed=31)
+    p.append_rope([0], [30], k, v, cos, sin)
+    ct, st = torch.from_numpy(cos).cuda(), torch.from_numpy(sin).cuda()
+    k2, v2 = _kv(11, hkv, d, seed=32)
+    with pytest.raises(kv4.KV4Error) as e:
+        p.gpu.append_rope([0], [11], k2, v2, ct, st)          # position 40 is beyond the tables
+    assert e.value.name == "KV4_ERR_INVALID_ARGUMENT"
+    assert p.gpu.seq_length(0) == 30
+    cfg = kv4.Config(num_q_heads=hq, num_kv_heads=hkv, head_dim=d, num_pages=8, max_seqs=2, max_pages_per_seq=4,
+                     num_sinks=0, num_recent=0, hadamard_block=1, format=kv4.FORMAT_BF16)
+    c = kv4.Cache(cfg, "cuda")
+    with pytest.raises(kv4.KV4Error) as e:
+        c.append_rope([0], [5], k2[:5].contiguous(), v2[:5].contiguous(), ct, st)
+    assert e.value.name == "KV4_ERR_UNSUPPORTED"
+    assert p.compare_cache([0]) > 0
+
+
+@pytest.mark.parametrize("fmt,b", [(kv4.FORMAT_INT4_PROT, 128), (kv4.FORMAT_BF16, 1)])
+def test_decode_bf16_output(fmt, b):
+    """bf16 output = round-to-nearest-even of the fp32 output of the same call, bit for bit; and
+    within the tolerance plus half a bf16 ulp of the oracle."""
+    _print_case("decode_bf16", fmt=fmt)
+    hq, hkv, d = 32, 8, 128
+    lens = [1, 40, 133, 700, 2000]
+    p = Pair(hq, hkv, d, num_pages=1024, max_seqs=8, max_pps=160, S=4, R=128, b=b, fmt=fmt)
+    ks, vs = zip(*[_kv(L, hkv, d, seed=41, idx=i) for i, L in enumerate(lens)])
+    p.append(list(range(len(lens))), lens, torch.cat(ks).contiguous(), torch.cat(vs).contiguous())
+    q = W.queries(len(lens), hq, d, 43, device="cuda")
+    ids = list(range(len(lens)))
+    o32, ref = p.decode(ids, q)
+    o16 = p.gpu.decode_attention_bf16(ids, q)
+    torch.cuda.synchronize()
+    bits16 = o16.view(torch.int16).cpu().numpy().astype(np.uint16)
+    assert np.array_equal(bits16, W.bf16_bits(torch.from_numpy(o32.astype(np.float32)).to(torch.bfloat16)))
+    v16 = (bits16.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    assert np.all(np.abs(v16 - ref) <= TOL + np.abs(ref) * 2.0 ** -8)
