@@ -48,7 +48,12 @@ def build(verbose: bool = False) -> str:
     kobjs = []
     for src in KERNEL_SOURCES:
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-        _run([hipcc, "--offload-arch=" + ARCH, *HIPFLAGS, *inc, "-c", os.path.join(CSRC, src), "-o", obj])
+        # the compiler's per-kernel resource report (registers, scratch, occupancy) is kept beside
+        # the object; a CPU test checks that no kernel uses scratch memory
+        out = _run([hipcc, "--offload-arch=" + ARCH, *HIPFLAGS, *inc, "-Rpass-analysis=kernel-resource-usage", "-c",
+                    os.path.join(CSRC, src), "-o", obj])
+        with open(os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".resources.txt"), "w") as f:
+            f.write(out)
         kobjs.append(obj)
     hobj = os.path.join(BUILD_DIR, "kv4_host.o")
     rocm = os.environ.get("ROCM_PATH", "/opt/rocm")

@@ -3,6 +3,7 @@
 the host planner (FIFO page allocator, block tables, append tasks, decode work list) agrees with the
 oracle's allocator on seeded random call sequences.  No GPU call is made."""
 import ctypes
+import glob
 import math
 import os
 import re
@@ -263,3 +264,35 @@ def test_planner_out_of_pages_changes_nothing(driver):
     assert pl.cmd("append 2 1 80 2 32", True)[0] == ["status", "0"]     # 5 + 2 = 7
     assert pl.cmd("freepages")[0] == ["free", "0"]
     pl.close()
+
+
+def _resource_reports():
+    """Per-kernel (VGPRs, scratch bytes per lane, occupancy) from the compiler's reports that
+    int4_kv_cache_fwht_amd/build.py keeps beside each kernel object."""
+    out = {}
+    for path in glob.glob(os.path.join(ROOT, "int4_kv_cache_fwht_amd", "_build", "*.resources.txt")):
+        name = None
+        for line in open(path):
+            m = re.search(r"Function Name: (\S+)", line)
+            if m:
+                name = m.group(1)
+                out[name] = {}
+                continue
+            for key, pat in (("vgprs", r"\bVGPRs: (\d+)"), ("scratch", r"ScratchSize \[bytes/lane\]: (\d+)"),
+                             ("occupancy", r"Occupancy \[waves/SIMD\]: (\d+)")):
+                m = re.search(pat, line)
+                if m and name:
+                    out[name][key] = int(m.group(1))
+    return out
+
+
+def test_kernels_use_no_scratch(libkv4):
+    """No kernel spills registers to scratch (private) memory, and the two hot split kernels keep
+    at least 2 waves per SIMD (their latency hiding depends on it)."""
+    rep = _resource_reports()
+    assert len(rep) >= 40, sorted(rep)[:5]
+    spills = {k: v for k, v in rep.items() if v.get("scratch", 0) != 0}
+    assert not spills, spills
+    for k, v in rep.items():
+        if "decode_split_kernel" in k or "mq_split_kernel" in k:
+            assert v["occupancy"] >= 2, (k, v)
