@@ -72,6 +72,16 @@ def _check_workload(name, sample_fn, positions_per_seq=12):
     print(name, "sampled sequences", sample, "lengths", [lens0[i] + 1 for i in sample], "max-abs", err,
           "oracle threads", used, flush=True)
     assert err <= TOL
+    # multi-query attention over the same cache: the last 4 positions of every sequence as causal
+    # query rows, one call (its own work split); the oracle checks the sampled sequences
+    nq = 4
+    qm = W.queries(nq * len(lens0), hq, d, w.seed, step=99, device=dev)
+    outm = cache.multi_query_attention(list(range(len(lens0))), [nq] * len(lens0), qm).cpu().numpy()
+    rows = np.concatenate([np.arange(nq * i, nq * (i + 1)) for i in sample])
+    refm, _ = ora.attend_multi(list(range(len(sample))), [nq] * len(sample), bf16_bits(qm[torch.from_numpy(rows).to(dev)]))
+    errm = np.abs(outm[rows].astype(np.float64) - refm).max()
+    print(name, "multi-query (4 rows) sampled max-abs", errm, flush=True)
+    assert errm <= TOL
     # codes and scales of sampled positions, bit for bit
     sz = cache.sizes
     pool = cache.page_pool.cpu().numpy()[: sz.page_pool].reshape(cache.cfg.num_pages, hkv, sz.page_block_bytes)
