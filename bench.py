@@ -313,8 +313,8 @@ def copy_probe(device):
 
 def append_workload(device, repeats=7):
     """The append path alone: 256 empty sequences x 512 single-position steps, and a bulk prefill of
-    32768 positions into one sequence, timed with the rotation (b = 128) and without it (b = 1,
-    plain INT4).  Returns the JSON record."""
+    32768 positions into one sequence, timed with the rotation (b = 128), without it (b = 1, plain
+    INT4), and with the fused RoPE of pre-RoPE keys (b = 128).  Returns the JSON record."""
     import torch
     import int4_kv_cache_fwht_amd as kv4
     import kv4_inputs as W
@@ -324,44 +324,52 @@ def append_workload(device, repeats=7):
     ch = W.outlier_channels(hkv, d, w.outlier_channels, w.seed)
     rows = [W.seq_kv(hkv, d, B, ch, w.outlier_scale, w.seed, 2000 + s, 0, device) for s in range(steps)]
     kb, vb = W.seq_kv(hkv, d, bulk, ch, w.outlier_scale, w.seed, 3000, 0, device)
+    cos, sin = (torch.from_numpy(t).to(device) for t in W.rope_tables(bulk + 1, d))
     res = {}
-    for block in (128, 1):
+    for name, block, rope in (("b128", 128, False), ("b1", 1, False), ("b128_rope", 128, True)):
         cfg = kv4.Config(num_q_heads=hq, num_kv_heads=hkv, head_dim=d, num_pages=B * (steps // 16) + bulk // 16 + 16,
                          max_seqs=B + 1, max_pages_per_seq=bulk // 16 + 1, num_sinks=w.num_sinks,
                          num_recent=w.num_recent, hadamard_block=block, format=0)
+
+        def app(cache, ids, n, k, v):
+            if rope:
+                cache.append_rope(ids, n, k, v, cos, sin)
+            else:
+                cache.append(ids, n, k, v)
+
         best_steps = best_bulk = float("inf")
         for _ in range(repeats):
             cache = kv4.Cache(cfg, device)
             ids = list(range(B))
-            cache.append(ids, [1] * B, rows[0][0], rows[0][1])  # warm-up of the launch path
+            app(cache, ids, [1] * B, rows[0][0], rows[0][1])  # warm-up of the launch path
             torch.cuda.synchronize()
-            cache.seq_free(0)
-            for i in ids[1:]:
+            for i in ids:
                 cache.seq_free(i)
             cache.profile_enable(True)
             for s in range(steps):
-                cache.append(ids, [1] * B, rows[s][0], rows[s][1])
+                app(cache, ids, [1] * B, rows[s][0], rows[s][1])
             p = cache.profile_read()
             best_steps = min(best_steps, p["append_ms"] / p["append_launches"] * 1e3)
             cache.profile_enable(True)
-            cache.append([B], [bulk], kb, vb)
+            app(cache, [B], [bulk], kb, vb)
             p = cache.profile_read()
             best_bulk = min(best_bulk, p["append_ms"] * 1e3)
             cache.profile_enable(False)
             del cache
-        res[block] = (best_steps, best_bulk)
-    (s128, b128), (s1, b1) = res[128], res[1]
+        res[name] = (best_steps, best_bulk)
+    (s128, b128), (s1, b1), (sr, br) = res["b128"], res["b1"], res["b128_rope"]
     bulk_bytes = bulk * hkv * d * 2 * 2 + bulk * hkv * 2 * (d // 2 + 4)   # bf16 in, INT4 + scales out
     return {"metric": "INT4 KV append (rotation + quantization + pack) tokens/s", "value": B / (s128 * 1e-6),
             "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": 1, "ms_per_step": s128 * 1e-3,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
             "config": {"workload": "append", "sequences": B, "steps": steps, "bulk_prefill": bulk, "kv_heads": hkv,
                        "head_dim": d, "sinks": w.num_sinks, "recent": w.num_recent},
-            "append_step_us": {"b128": s128, "b1": s1, "rotation_overhead": s128 / s1 - 1.0},
+            "append_step_us": {"b128": s128, "b1": s1, "rotation_overhead": s128 / s1 - 1.0,
+                               "b128_fused_rope": sr, "fused_rope_overhead": sr / s128 - 1.0},
             "bulk_prefill_us": {"b128": b128, "b1": b1, "rotation_overhead": b128 / b1 - 1.0,
-                                "GBps_b128": bulk_bytes / (b128 * 1e-6) / 1e9},
+                                "GBps_b128": bulk_bytes / (b128 * 1e-6) / 1e9, "b128_fused_rope": br,
+                                "fused_rope_overhead": br / b128 - 1.0},
             "note": "best of %d repeats; kernel time from HIP events on the call's stream" % repeats}
-
 
 def mq_workload(device, n_q, steps, warmup, n_caches=4):
     """Multi-query attention on the Qwen3-8B-shaped layer (64 sequences, lengths uniform in
