@@ -393,7 +393,7 @@ __global__ __launch_bounds__(64) void append_token_kernel(AppendArgs a)
 #pragma unroll
         for (int j = 0; j < PL; j++) {
             const float own = y[j];
-            const float other = __shfl_xor(own, 16, 64);
+            const float other = lane_xor16(own);
             const float oc = own * cr[j], os = other * sr[j];
             const float r = (l32 & 16) ? oc + os : oc - os;
             y[j] = row == 0 ? r : own;
@@ -413,14 +413,18 @@ __global__ __launch_bounds__(64) void append_token_kernel(AppendArgs a)
             }
         }
     }
-    for (int hh = PL; hh < a.block; hh <<= 1) {
-        const int m = hh / PL;
+    // then the stages h = PL * M < b across lanes: partner lane l ^ M (M <= 16 stays in the row's
+    // 32 lanes), DPP moves and one swizzle instead of LDS permutes
+    static_for<0, 5>([&](auto S) {
+        constexpr int M = 1 << S;
+        if (M * PL < a.block) {
 #pragma unroll
-        for (int i = 0; i < PL; i++) {
-            const float other = __shfl_xor(y[i], m, 64);
-            y[i] = (l32 & m) ? other - y[i] : y[i] + other;
+            for (int i = 0; i < PL; i++) {
+                const float other = lane_xor<M>(y[i]);
+                y[i] = (l32 & M) ? other - y[i] : y[i] + other;
+            }
         }
-    }
+    });
     if (a.block > 1) {
 #pragma unroll
         for (int i = 0; i < PL; i++) y[i] = y[i] * a.cb;
@@ -432,11 +436,11 @@ __global__ __launch_bounds__(64) void append_token_kernel(AppendArgs a)
         mn = fminf(mn, y[i]);
         mx = fmaxf(mx, y[i]);
     }
-#pragma unroll
-    for (int m = 1; m < 32; m <<= 1) {
-        mn = fminf(mn, __shfl_xor(mn, m, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, m, 64));
-    }
+    static_for<0, 5>([&](auto S) {
+        constexpr int M = 1 << S;
+        mn = fminf(mn, lane_xor<M>(mn));
+        mx = fmaxf(mx, lane_xor<M>(mx));
+    });
 
     // ---- INT8 codes: protected position, or INT4 re-quantized from the INT8 round trip ----
     const int t = tk.t0;
@@ -460,11 +464,11 @@ __global__ __launch_bounds__(64) void append_token_kernel(AppendArgs a)
             mn = fminf(mn, y[i]);
             mx = fmaxf(mx, y[i]);
         }
-#pragma unroll
-        for (int m = 1; m < 32; m <<= 1) {
-            mn = fminf(mn, __shfl_xor(mn, m, 64));
-            mx = fmaxf(mx, __shfl_xor(mx, m, 64));
-        }
+        static_for<0, 5>([&](auto S) {
+            constexpr int M = 1 << S;
+            mn = fminf(mn, lane_xor<M>(mn));
+            mx = fmaxf(mx, lane_xor<M>(mx));
+        });
     }
 
     // ---- INT4 page copy ----

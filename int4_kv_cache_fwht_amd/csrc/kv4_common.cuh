@@ -82,18 +82,62 @@ __device__ __forceinline__ float dpp_xor1(float x)
     return as_float((uint32_t)__builtin_amdgcn_update_dpp(0, (int)as_uint(x), 0xB1, 0xF, 0xF, false));
 }
 
-__device__ __forceinline__ float wave_max(float x)
+// Value of lane l ^ M of x within each row of 16 lanes (M = 1, 2, 4, 8), by DPP moves (no LDS
+// access): 1 and 2 are quad permutations; 4 is row_half_mirror (l ^ 7) followed by quad_perm
+// [3,2,1,0] (l ^ 3); 8 rotates the row by 8.
+template <int M>
+__device__ __forceinline__ float lane_xor_row(float x)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-    return x;
+    static_assert(M == 1 || M == 2 || M == 4 || M == 8, "a partner inside the row");
+    const int v = (int)as_uint(x);
+    int r;
+    if constexpr (M == 1) {
+        r = __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false);
+    } else if constexpr (M == 2) {
+        r = __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false);
+    } else if constexpr (M == 4) {
+        const int t = __builtin_amdgcn_update_dpp(v, v, 0x141, 0xF, 0xF, false);
+        r = __builtin_amdgcn_update_dpp(t, t, 0x1B, 0xF, 0xF, false);
+    } else {
+        r = __builtin_amdgcn_update_dpp(v, v, 0x128, 0xF, 0xF, false);
+    }
+    return as_float((uint32_t)r);
 }
 
-__device__ __forceinline__ float wave_sum(float x)
+// Value of lane l ^ 16 within each half of the wave (ds_swizzle in bit mode, and-mask 0x1F,
+// xor-mask 0x10: no address computation).
+__device__ __forceinline__ float lane_xor16(float x)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
-    return x;
+    return as_float((uint32_t)__builtin_amdgcn_ds_swizzle((int)as_uint(x), 0x401F));
+}
+
+// Value of lane l ^ M for a power of two M < 64 (every lane active).
+template <int M>
+__device__ __forceinline__ float lane_xor(float x)
+{
+    if constexpr (M <= 8)
+        return lane_xor_row<M>(x);
+    else if constexpr (M == 16)
+        return lane_xor16(x);
+    else
+        return __shfl_xor(x, M, 64);
+}
+
+// x[l] + x[l ^ 32] and max(x[l], x[l ^ 32]).  v_permlane32_swap of x with itself leaves the two
+// values of the pair, one in each result, on every lane; a sum or max of the two is the same bits
+// whichever result holds which.
+__device__ __forceinline__ float add_xor32(float x)
+{
+    const int v = (int)as_uint(x);
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return as_float((uint32_t)r[0]) + as_float((uint32_t)r[1]);
+}
+
+__device__ __forceinline__ float max_xor32(float x)
+{
+    const int v = (int)as_uint(x);
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return fmaxf(as_float((uint32_t)r[0]), as_float((uint32_t)r[1]));
 }
 
 // LDS written by some lanes of a wave and then read by other lanes of the same wave: the LDS

@@ -69,18 +69,19 @@ __device__ __forceinline__ const __attribute__((address_space(4))) T* kernarg_fi
                                                             __builtin_amdgcn_kernarg_segment_ptr() + offset);
 }
 
-// Steps of one (entry, kv head) unit at length L (the host planner's rule).
+// Global steps of one (entry, kv head) unit at length L, the start charge included (the host
+// planner's rule).
 template <int FMT>
 __device__ __forceinline__ int unit_steps_dev(const DecodeArgs& a, int L, int n8)
 {
     if (FMT == FMT_INT4_PROT) {
         const int lo = a.sinks, hi = L - a.recent;
         const int pages = hi > lo ? (hi - 1) / kPageSize + 1 - lo / kPageSize : 0;
-        return n8 + (pages + kInt4StepPages - 1) / kInt4StepPages;
+        return kUnitStartSteps + n8 + (pages + kInt4StepPages - 1) / kInt4StepPages;
     }
     const int pages = (L + kPageSize - 1) / kPageSize;
-    if (FMT == FMT_INT8) return (pages + kInt8StepPages - 1) / kInt8StepPages;
-    return pages;
+    if (FMT == FMT_INT8) return kUnitStartSteps + (pages + kInt8StepPages - 1) / kInt8StepPages;
+    return kUnitStartSteps + pages;
 }
 
 // Argument plan held in registers: lane l holds entries l + 64 j (first global step, sequence id,
@@ -247,16 +248,19 @@ struct DecodeWave {
 #pragma unroll
             for (int j = 0; j < NHV; j++) qv[i][j] = as_float((uint32_t)raw[i * D + 64 * j + lane] << 16);
         wave_lds_sync();
-        // block FWHT in fp32 (any stage order)
-        for (int hh = 1; hh < a.block && hh < 64; hh <<= 1) {
+        // block FWHT in fp32 (any stage order); partner lane l ^ H by DPP, swizzle or permute
+        static_for<0, 6>([&](auto S) {
+            constexpr int H = 1 << S;
+            if (H < a.block) {
 #pragma unroll
-            for (int i = 0; i < G; i++)
+                for (int i = 0; i < G; i++)
 #pragma unroll
-                for (int j = 0; j < NHV; j++) {
-                    const float other = __shfl_xor(qv[i][j], hh, 64);
-                    qv[i][j] = (lane & hh) ? other - qv[i][j] : qv[i][j] + other;
-                }
-        }
+                    for (int j = 0; j < NHV; j++) {
+                        const float other = lane_xor<H>(qv[i][j]);
+                        qv[i][j] = (lane & H) ? other - qv[i][j] : qv[i][j] + other;
+                    }
+            }
+        });
         if constexpr (NHV > 1) {
             if (a.block > 64) {
 #pragma unroll
@@ -609,7 +613,7 @@ struct DecodeWave {
         });
         float4_t S = (S4[0] + S4[1]) + (S4[2] + S4[3]);
 #pragma unroll
-        for (int i = 0; i < 4; i++) S[i] = S[i] + __shfl_xor(S[i], 32, 64);
+        for (int i = 0; i < 4; i++) S[i] = add_xor32(S[i]);
 
         const float sK = f16_bits_to_float(b.sz.x & 0xFFFFu), zK = f16_bits_to_float(b.sz.x >> 16);
         const float sV = f16_bits_to_float(b.sz.y & 0xFFFFu), zV = f16_bits_to_float(b.sz.y >> 16);
@@ -699,6 +703,16 @@ struct DecodeWave {
         }
     }
 
+    // Work steps [k0, k1) of unit U inside the wave's slice [s, s_end): the unit's global range
+    // [step_begin, ue) opens with kUnitStartSteps steps without work (empty when the slice covers
+    // only those).
+    __device__ __forceinline__ void unit_slice(const DecodeUnit& U, int64_t ue, int64_t s, int& k0, int& k1) const
+    {
+        const int64_t wb = U.step_begin + kUnitStartSteps;
+        k0 = (int)(s > wb ? s - wb : 0);
+        k1 = (int)((s_end < ue ? s_end : ue) - wb);
+    }
+
     // ---- the wave's steps [s, s_end), starting in unit u (quantized formats) ----
     __device__ void run(int u, int64_t s)
     {
@@ -706,11 +720,13 @@ struct DecodeWave {
             DecodeUnit U;
             int64_t ue;
             unit_at(u, U, ue);
-            const int k0 = (int)(s - U.step_begin);
-            const int k1 = (int)((s_end < ue ? s_end : ue) - U.step_begin);
-            run_unit(U, k0, k1);
-            epilogue(w + u);
-            s = U.step_begin + k1;
+            int k0, k1;
+            unit_slice(U, ue, s, k0, k1);
+            if (k1 > k0) {
+                run_unit(U, k0, k1);
+                epilogue(w + u);
+            }
+            s = ue;
             u++;
         }
         wait_vm_all();
@@ -843,12 +859,14 @@ struct DecodeWave {
             DecodeUnit U;
             int64_t ue;
             unit_at(u, U, ue);
-            const int k0 = (int)(s - U.step_begin);
-            const int k1 = (int)((s_end < ue ? s_end : ue) - U.step_begin);
-            prologue_bf16(U);
-            for (int k = k0; k < k1; k++) bf16_step(U, k);
-            epilogue(w + u);
-            s = U.step_begin + k1;
+            int k0, k1;
+            unit_slice(U, ue, s, k0, k1);
+            if (k1 > k0) {
+                prologue_bf16(U);
+                for (int k = k0; k < k1; k++) bf16_step(U, k);
+                epilogue(w + u);
+            }
+            s = ue;
             u++;
         }
     }
@@ -921,7 +939,8 @@ __global__ __launch_bounds__(64 * G) void merge_kernel(DecodeArgs a)
         se = (u + 1 < a.n_units) ? ld_uniform(&a.units[u + 1].step_begin) : a.total_steps;
     }
     const int64_t T = a.total_steps, W = a.n_waves;
-    const int64_t sb = U.step_begin;
+    // the waves whose slices hold work steps of the unit (after its start charge)
+    const int64_t sb = U.step_begin + kUnitStartSteps;
     const int64_t w0 = wave_of_step(sb, T, W), w1 = wave_of_step(se - 1, T, W);
     const int n = (int)(w1 - w0 + 1);
     // partial j of this unit sits at index w0 + u + j; (m, l) are read with scalar loads (the split
@@ -947,13 +966,16 @@ __global__ __launch_bounds__(64 * G) void merge_kernel(DecodeArgs a)
 #pragma unroll
     for (int hv = 0; hv < NHV; hv++) r[hv] = (Ls > 0.f) ? O[hv] / Ls : 0.f;
     if (ROT && a.block > 1) {
-        for (int hh = 1; hh < a.block && hh < 64; hh <<= 1) {
+        static_for<0, 6>([&](auto S) {
+            constexpr int H = 1 << S;
+            if (H < a.block) {
 #pragma unroll
-            for (int hv = 0; hv < NHV; hv++) {
-                const float other = __shfl_xor(r[hv], hh, 64);
-                r[hv] = (lane & hh) ? other - r[hv] : r[hv] + other;
+                for (int hv = 0; hv < NHV; hv++) {
+                    const float other = lane_xor<H>(r[hv]);
+                    r[hv] = (lane & H) ? other - r[hv] : r[hv] + other;
+                }
             }
-        }
+        });
         if constexpr (NHV > 1) {
             if (a.block > 64) {
                 const float a0 = r[0], a1 = r[1];

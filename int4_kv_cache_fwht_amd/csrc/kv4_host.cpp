@@ -87,11 +87,13 @@ struct Profiler {
     std::vector<std::vector<hipEvent_t>> mq_ev;     // the same for multi-query calls
     kv4_profile totals{};
 
+    // Timing-only events: no system-scope fence when they are recorded, so the measured interval
+    // holds the kernel and its dispatch, not a writeback of the caches to the host's view.
     static hipError_t make(int n, std::vector<hipEvent_t>* out)
     {
         out->assign((size_t)n, nullptr);
         for (auto& e : *out) {
-            hipError_t r = hipEventCreate(&e);
+            hipError_t r = hipEventCreateWithFlags(&e, hipEventDisableSystemFence);
             if (r != hipSuccess) return r;
         }
         return hipSuccess;

@@ -20,9 +20,10 @@
 // lane l supplies to the PV operand, and whose value codes are one 4-byte (INT4) or 8-byte (INT8)
 // run of each dim row.  The two products therefore need no exchange between lanes.
 //
-// Softmax reference: per query row, the running maximum of score + (exponent field of s_V); it is
-// raised only when a step exceeds it by more than kMqTau (then the accumulators are rescaled).
-// This bounds p * s_V * 2^27 below 2^14, inside the fp16 range, whatever the value scales.
+// Softmax reference: per query row, the running maximum of score + (exponent field of s_V, the
+// largest over a lane's positions); it is raised only when a step exceeds it by more than kMqTau
+// (then the accumulators are rescaled).  This bounds p * s_V * 2^27 below 2^14, inside the fp16
+// range, whatever the value scales.
 #include "kv4_common.cuh"
 
 namespace kv4 {
@@ -178,18 +179,17 @@ struct MqWave {
                 }
             }
         }
-#pragma unroll
-        for (int st = 0; st < 2; st++) {
-            if ((DPL << st) < a.block) {
-                const int mask = 16 << st;
-                const bool upper = (lane & mask) != 0;
+        static_for<0, 2>([&](auto ST) {
+            constexpr int MASK = 16 << ST;
+            if ((DPL << ST) < a.block) {
+                const bool upper = (lane & MASK) != 0;
 #pragma unroll
                 for (int i = 0; i < DPL; i++) {
-                    const float o = __shfl_xor(x[i], mask, 64);
+                    const float o = lane_xor<MASK>(x[i]);
                     x[i] = upper ? o - x[i] : x[i] + o;
                 }
             }
-        }
+        });
         float sum = 0.f, mx = 0.f;
 #pragma unroll
         for (int i = 0; i < DPL; i++) {
@@ -197,10 +197,10 @@ struct MqWave {
             sum += x[i];
             mx = fmaxf(mx, fabsf(x[i]));
         }
-        sum += __shfl_xor(sum, 16, 64);
-        sum += __shfl_xor(sum, 32, 64);
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        sum += lane_xor16(sum);
+        sum = add_xor32(sum);
+        mx = fmaxf(mx, lane_xor16(mx));
+        mx = max_xor32(mx);
         const int E = __builtin_amdgcn_frexp_expf(mx); // mx < 2^E
 #pragma unroll
         for (int j = 0; j < KS; j++) {
@@ -361,21 +361,26 @@ struct MqWave {
             sa = mfma16x32(ka, qlo[j], sa);
             sb = mfma16x32(kb, qlo[j], sb);
         }
-        // fp16 scales enter the fp32 arithmetic as fma operands (v_fma_mix_f32: no conversions)
-        float st[8], w[8];
+        // fp16 scales enter the fp32 arithmetic as fma operands (v_fma_mix_f32: no conversions).
+        // The reference bound uses one exponent per lane: the largest s_V of the lane's readable
+        // positions (positive fp16 patterns order like their values), so st + e_lane bounds
+        // st + log2 s_V + 1 for each of them.
+        float st[8];
         bool ok[8];
-        float wmax = -__builtin_inff();
+        float smax = -__builtin_inff();
+        uint32_t svmax = 0;
 #pragma unroll
         for (int t = 0; t < 8; t++) {
             const float r = t < 4 ? sa[t] : sb[t - 4];
             const uint32_t d0 = b.sc[2 * t], d1 = b.sc[2 * t + 1];
             st[t] = fmaf(lo_half(d0), r * Ar, fmaf(hi_half(d0), Br, 0.f));
             ok[t] = FULL || pos[t] <= pos_r;
-            w[t] = ok[t] ? st[t] + (float)((d1 >> 10) & 31u) : -__builtin_inff();
-            wmax = fmaxf(wmax, w[t]);
+            smax = ok[t] ? fmaxf(smax, st[t]) : smax;
+            svmax = ok[t] ? max(svmax, d1 & 0xFFFFu) : svmax;
         }
-        wmax = fmaxf(wmax, __shfl_xor(wmax, 16, 64));
-        wmax = fmaxf(wmax, __shfl_xor(wmax, 32, 64));
+        float wmax = smax + (float)(svmax >> 10);
+        wmax = fmaxf(wmax, lane_xor16(wmax));
+        wmax = max_xor32(wmax);
         const bool need = wmax > m_ref + kMqTau;
         if (__builtin_amdgcn_ballot_w64(need)) {
             const float f = need ? __builtin_amdgcn_exp2f(m_ref - wmax) : 1.f;
@@ -457,10 +462,10 @@ struct MqWave {
 
     __device__ void finish(int task)
     {
-        lsum += __shfl_xor(lsum, 16, 64);
-        lsum += __shfl_xor(lsum, 32, 64);
-        zsum += __shfl_xor(zsum, 16, 64);
-        zsum += __shfl_xor(zsum, 32, 64);
+        lsum += lane_xor16(lsum);
+        lsum = add_xor32(lsum);
+        zsum += lane_xor16(zsum);
+        zsum = add_xor32(zsum);
         if (g == 0) {
             float* ml = a.part_ml + ((int64_t)task * kMqRows + n) * 2;
             ml[0] = m_ref;
@@ -588,17 +593,17 @@ __global__ __launch_bounds__(256) void mq_merge_kernel(MqArgs a)
             o[0] = u + w;
             o[DPM - 1] = u - w;
         }
-#pragma unroll
-        for (int m = 1; m < 64; m <<= 1) {
-            if (m * DPM < a.block) {
-                const bool upper = (lane & m) != 0;
+        static_for<0, 6>([&](auto S) {
+            constexpr int M = 1 << S;
+            if (M * DPM < a.block) {
+                const bool upper = (lane & M) != 0;
 #pragma unroll
                 for (int k = 0; k < DPM; k++) {
-                    const float other = __shfl_xor(o[k], m, 64);
+                    const float other = lane_xor<M>(o[k]);
                     o[k] = upper ? other - o[k] : o[k] + other;
                 }
             }
-        }
+        });
 #pragma unroll
         for (int k = 0; k < DPM; k++) o[k] *= a.cb;
     }

@@ -110,7 +110,8 @@ inline void unit_int4_pages(const Config& c, int L, int* p0, int* p1)
     *p1 = (hi - 1) / kPageSize + 1;
 }
 
-inline int unit_steps(const Config& c, int L)
+// Decode steps of one (entry, kv head) unit that read the cache.
+inline int unit_work_steps(const Config& c, int L)
 {
     if (c.format == FMT_INT4_PROT) {
         int p0, p1;
@@ -121,6 +122,9 @@ inline int unit_steps(const Config& c, int L)
     if (c.format == FMT_INT8) return (pages + kInt8StepPages - 1) / kInt8StepPages;
     return pages; // bf16: one page per step
 }
+
+// The unit's share of the global step range: its start charge, then its work steps.
+inline int unit_steps(const Config& c, int L) { return kUnitStartSteps + unit_work_steps(c, L); }
 
 // Multi-query attention steps of one (sequence, kv head): INT4_PROT reads its INT8 protection
 // tiles two at a time, then the INT4 pages of [S, L - R) two at a time; the INT8 format reads its

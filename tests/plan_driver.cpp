@@ -10,8 +10,9 @@
 //   free id                      -> "status S"
 //   bt id                        -> "bt LEN p0 p1 ..." (the sequence's pages, in order)
 //   freepages                    -> "free N"
-//   decode n id0 id1 ...         -> "status S total T", then one "unit seq len entry head step_begin"
-//                                   line per unit, then "end"
+//   decode n id0 id1 ...         -> "status S total T start C" (C = the start charge of every unit's
+//                                   step range), then one "unit seq len entry head step_begin" line
+//                                   per unit, then "end"
 //   sizes                        -> "sizes page_pool int8_pool block_table page_block int8_tile int8_tiles"
 //   multi target n id0 nq0 ...   -> "status S tasks T groups G spc C n8 N8", then one
 //                                   "entry seq len nq qrow0 task0 grp0 steps nch" line per entry, "end"
@@ -94,7 +95,7 @@ int main()
             std::vector<kv4::DecodeUnit> units;
             int64_t total = 0;
             kv4::Status s = st.plan_decode(n, ids.data(), &units, &total, nullptr);
-            std::printf("status %d total %lld\n", (int)s, (long long)total);
+            std::printf("status %d total %lld start %d\n", (int)s, (long long)total, kv4::kUnitStartSteps);
             if (s == kv4::OK)
                 for (const auto& u : units)
                     std::printf("unit %d %d %d %d %lld\n", u.seq, u.len, u.entry, u.head, (long long)u.step_begin);

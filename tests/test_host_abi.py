@@ -221,7 +221,7 @@ def test_planner_matches_oracle_allocator(driver, seed, S, R, fmt):
                 assert int(hdr[1]) == 3
                 continue
             assert int(hdr[1]) == 0
-            _check_units(units, ids, lens, hkv, S, R, fmt, int(hdr[3]))
+            _check_units(units, ids, lens, hkv, S, R, fmt, int(hdr[3]), int(hdr[5]))
         assert int(pl.cmd("freepages")[0][1]) == ora.free_pages()
         for sid in range(max_seqs):
             b = pl.cmd("bt %d" % sid)[0]
@@ -230,10 +230,12 @@ def test_planner_matches_oracle_allocator(driver, seed, S, R, fmt):
     pl.close()
 
 
-def _check_units(units, ids, lens, hkv, S, R, fmt, total):
-    """One unit per (entry, kv head), entry-major, with step ranges that tile [0, total).  The INT4
-    steps of a protected-format unit cover the pages of every unprotected position at 4 pages a step;
-    its INT8 steps cover the S + R protection slots at 32 a step."""
+def _check_units(units, ids, lens, hkv, S, R, fmt, total, start):
+    """One unit per (entry, kv head), entry-major, with step ranges that tile [0, total).  Each range
+    is the start charge (`start` steps without work, a small constant) and then the work steps: the
+    INT4 steps of a protected-format unit cover the pages of every unprotected position at 4 pages a
+    step; its INT8 steps cover the S + R protection slots at 32 a step."""
+    assert 0 <= start <= 8
     assert len(units) == len(ids) * hkv
     pos = 0
     for e, sid in enumerate(ids):
@@ -250,7 +252,7 @@ def _check_units(units, ids, lens, hkv, S, R, fmt, total):
         for h in range(hkv):
             seq, ln, entry, head, begin = units[e * hkv + h]
             assert (seq, ln, entry, head, begin) == (sid, L, e, h, pos)
-            pos += steps
+            pos += start + steps
     assert pos == total
 
 
