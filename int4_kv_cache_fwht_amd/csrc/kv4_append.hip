@@ -184,9 +184,10 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a)
         // position when the INT4 codes are re-quantized from the INT8 round trip ----
         const bool want8 = (FMT == FMT_INT8) ? active : prot;
         const bool requant = (FMT == FMT_INT4_PROT) && a.requant != 0;
+        const bool any8 = __ballot(want8) != 0ull; // some row of the page gets INT8 codes
         QuantParams qp8 = {};
         uint32_t cb8[N / 4];
-        if (requant || __ballot(want8) != 0ull) {
+        if (requant || any8) {
             qp8 = quant_params(mn, mx, 255.0f);
 #pragma unroll
             for (int q = 0; q < N / 4; q++) {
@@ -288,33 +289,58 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a)
         }
         __syncthreads();
 
-        // ---- dim-major V stores: lane = dim ----
+        if constexpr (FMT == FMT_INT4_PROT) {
+            // ---- dim-major V, [D][8 B] with nibble s = slot s: lane l < D/2 takes dims 2l and
+            // 2l + 1 (byte l of every staged row) and writes their 16 B at once ----
+            if (lane < D / 2) {
+                uint32_t e0 = 0u, e1 = 0u, o0 = 0u, o1 = 0u; // dim 2l: slots 0-7, 8-15; dim 2l + 1: the same
 #pragma unroll
-        for (int dd = 0; dd < D / 64; dd++) {
-            const int d = dd * 64 + lane;
-            if constexpr (FMT == FMT_INT4_PROT) {
-                // [D][8 B]: nibble s = slot s
-                u32x2* dst = (u32x2*)(pb + 8 * D + d * 8);
-                u32x2 w = (tk.n < 16) ? *dst : (u32x2){0u, 0u};
-                for (int s = s0; s < s1; s++) {
-                    uint32_t nib = (lds_v4[s * (D / 2) + (d >> 1)] >> ((d & 1) * 4)) & 0xFu;
-                    int sh = (s & 7) * 4;
-                    if (s < 8)
-                        w.x = (w.x & ~(0xFu << sh)) | (nib << sh);
-                    else
-                        w.y = (w.y & ~(0xFu << sh)) | (nib << sh);
+                for (int s = 0; s < kPageSize; s++) {
+                    const uint32_t b = lds_v4[s * (D / 2) + lane];
+                    const uint32_t lo = b & 0xFu, hi = b >> 4;
+                    if (s < 8) {
+                        e0 |= lo << (4 * s);
+                        o0 |= hi << (4 * s);
+                    } else {
+                        e1 |= lo << (4 * (s - 8));
+                        o1 |= hi << (4 * (s - 8));
+                    }
                 }
-                *dst = w;
-                // INT8 copies of protected positions: one byte per (position, dim)
-                for (int s = s0; s < s1; s++) {
-                    const int ts = tk.t0 - s0 + s;
-                    if (!is_protected(ts, tk.len_new, a.sinks, a.recent)) continue;
-                    const int u = (ts < a.sinks) ? ts : a.sinks + ts % a.recent;
-                    uint8_t* tb = a.int8_pool + (((int64_t)tk.seq * a.hkv + h) * a.int8_tiles + (u >> 4)) * a.int8_tile;
-                    // V of slot u % 16: block (u % 16) / 8, [D][8 B], byte (u % 8)
-                    tb[((u >> 3) & 1) * (16 * D + 128) + 8 * D + d * 8 + (u & 7)] = lds_v8[s * D + d];
+                u32x4* dst = (u32x4*)(pb + 8 * D + 16 * lane);
+                if (tk.n < kPageSize) {
+                    // a partial page keeps the nibbles of the slots outside [s0, s1) (the staged
+                    // rows of those slots were not written)
+                    const uint64_t m = (((uint64_t)1 << (4 * tk.n)) - 1u) << (4 * s0);
+                    const uint32_t mlo = (uint32_t)m, mhi = (uint32_t)(m >> 32);
+                    const u32x4 old = *dst;
+                    e0 = (old.x & ~mlo) | (e0 & mlo);
+                    e1 = (old.y & ~mhi) | (e1 & mhi);
+                    o0 = (old.z & ~mlo) | (o0 & mlo);
+                    o1 = (old.w & ~mhi) | (o1 & mhi);
                 }
-            } else {
+                *dst = (u32x4){e0, e1, o0, o1};
+            }
+            // ---- INT8 copies of protected positions (pages that hold one): one byte per
+            // (position, dim), lane = dim ----
+            if (any8) {
+#pragma unroll
+                for (int dd = 0; dd < D / 64; dd++) {
+                    const int d = dd * 64 + lane;
+                    for (int s = s0; s < s1; s++) {
+                        const int ts = tk.t0 - s0 + s;
+                        if (!is_protected(ts, tk.len_new, a.sinks, a.recent)) continue;
+                        const int u = (ts < a.sinks) ? ts : a.sinks + ts % a.recent;
+                        uint8_t* tb = a.int8_pool + (((int64_t)tk.seq * a.hkv + h) * a.int8_tiles + (u >> 4)) * a.int8_tile;
+                        // V of slot u % 16: block (u % 16) / 8, [D][8 B], byte (u % 8)
+                        tb[((u >> 3) & 1) * (16 * D + 128) + 8 * D + d * 8 + (u & 7)] = lds_v8[s * D + d];
+                    }
+                }
+            }
+        } else {
+            // ---- dim-major V stores (INT8 format): lane = dim ----
+#pragma unroll
+            for (int dd = 0; dd < D / 64; dd++) {
+                const int d = dd * 64 + lane;
                 // INT8 format: block x = slot / 8 holds V as [D][8 B], byte j = slot 8x + j
                 u32x2* dst0 = (u32x2*)(pb + 8 * D + d * 8);
                 u32x2* dst1 = (u32x2*)(pb + (16 * D + 128) + 8 * D + d * 8);
