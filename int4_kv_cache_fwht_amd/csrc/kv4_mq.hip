@@ -79,6 +79,20 @@ __device__ __forceinline__ u32x4 centre(u32x4 x)
     return r;
 }
 
+// Eight INT4 value codes in the spread order, centred: (nibble | 0x6400) is the fp16 value
+// 1024 + code, less 1024 + MID in one packed fp16 subtraction.  k6400 holds 0x64006400 in a
+// vector register, so that mask-and-or is one v_and_or_b32 (two literals cannot share it).
+template <int MID>
+__device__ __forceinline__ u32x4 spread_centre_int4(uint32_t w, uint32_t k6400)
+{
+    const half2_t off = {(_Float16)(-(1024 + MID)), (_Float16)(-(1024 + MID))};
+    u32x4 r;
+#pragma unroll
+    for (int s = 0; s < 4; s++)
+        r[s] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, ((w >> (4 * s)) & 0x000F000Fu) | k6400) + off);
+    return r;
+}
+
 // hi + lo fp16 of eight floats, same element order as the spreads.
 __device__ __forceinline__ void split_hilo(const float (&x)[8], u32x4& hi, u32x4& lo)
 {
@@ -141,12 +155,19 @@ struct MqWave {
     int ring_base, ring_mod; // INT4_PROT: first recent position and its residue mod R
     const uint8_t* t8;   // INT4_PROT: this (sequence, kv head)'s INT8 tiles
     const int32_t* btrow;
+    const uint8_t* hbase; // the pool at this kv head's block of page 0
+    uint32_t pstride;     // bytes from one page to the next (all kv heads' blocks)
     int p0, p1;          // INT4 page range (INT4_PROT) or page count (INT8 format: p1)
     float m_ref = -__builtin_inff(), lsum = 0.f, zsum = 0.f, Ar = 0.f, Br = 0.f;
+    uint32_t k6400;      // 0x64006400 in a vector register (identity DPP move: not a literal)
     u32x4 qhi[KS], qlo[KS];
     float4_t acc[NCB];
 
-    __device__ MqWave(const MqArgs& args, int l) : a(args), lane(l), n(l & 15), g(l >> 4) {}
+    __device__ MqWave(const MqArgs& args, int l)
+        : a(args), lane(l), n(l & 15), g(l >> 4),
+          k6400((uint32_t)__builtin_amdgcn_update_dpp(0, 0x64006400, 0xE4, 0xF, 0xF, false))
+    {
+    }
 
     // Rotated, scaled query row n: dims DPL*g .. DPL*g + DPL - 1 held by this lane.
     __device__ void prologue(const MqEntry& e, int rt)
@@ -220,13 +241,12 @@ struct MqWave {
     __device__ void load4(Buf<false>& b, int s) const
     {
         const int pi = p0 + 2 * (s - a.n8);
-        const int pa = mq_uniform(btrow + pi);
-        const int pb = mq_uniform(btrow + (pi + 1 < p1 ? pi + 1 : pi));
-        const uint8_t* A = a.pool + ((int64_t)pa * a.hkv + head) * a.page_block;
-        const uint8_t* B = a.pool + ((int64_t)pb * a.hkv + head) * a.page_block;
+        const uint32_t pa = (uint32_t)mq_uniform(btrow + pi);
+        const uint32_t pb = (uint32_t)mq_uniform(btrow + (pi + 1 < p1 ? pi + 1 : pi));
+        // the lane picks its page id first: one 32x32 -> 64-bit multiply-add per pointer
         const int kslot = 8 * ((n >> 2) & 1) + (n & 3);
-        const uint8_t* kp = pick(n < 8, A, B) + kslot * 16;
-        const uint8_t* vp = pick(g < 2, A, B);
+        const uint8_t* kp = hbase + (uint64_t)(n < 8 ? pa : pb) * pstride + kslot * 16;
+        const uint8_t* vp = hbase + (uint64_t)(g < 2 ? pa : pb) * pstride;
         if constexpr (D == 128) {
             kp += 256 * g;
 #pragma unroll
@@ -412,7 +432,8 @@ struct MqWave {
         split_hilo_rtz(P, phi, plo);
 #pragma unroll
         for (int c = 0; c < NCB; c++) {
-            const u32x4 bv = centre<MID>(IS8 ? spread_int8(b.v[c][0], b.v[c][1]) : spread_int4(b.v[c][0]));
+            const u32x4 bv = IS8 ? centre<MID>(spread_int8(b.v[c][0], b.v[c][1]))
+                                 : spread_centre_int4<MID>(b.v[c][0], k6400);
             acc[c] = mfma16x32(phi, bv, acc[c]);
             acc[c] = mfma16x32(plo, bv, acc[c]);
         }
@@ -516,6 +537,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     W.L = e.len;
     W.head = head;
     W.btrow = a.bt + (int64_t)e.seq * a.max_pps;
+    W.hbase = a.pool + (int64_t)head * a.page_block;
+    W.pstride = (uint32_t)(a.hkv * a.page_block);
     if (FMT == FMT_INT4_PROT) {
         W.lo4 = a.sinks;
         W.hi4 = e.len - a.recent;
