@@ -10,10 +10,11 @@
 // a chunk of that (sequence, kv head)'s steps.  A step is 32 positions: two INT8 tiles (the
 // protection slots, first) or two INT4 pages.  Both products run on v_mfma_f32_16x16x32_f16:
 //   S^T = K Q^T:  the A operand is 16 positions' key codes as fp16 subnormal patterns (value
-//                 code * 2^-24, exact); the B operand the rotated query rows, scaled by a power of
-//                 two and split into hi + lo fp16.  A score is s_K (q . code) + z_K sum(q).
-//   O += P' V:    the A operand is p * s_V (hi + lo fp16), the B operand the value codes, which
-//                 the page stores dim-major, centred (code - 8; INT8: - 128) as fp16 integers;
+//                 code * 2^-24, exact; INT4 odd elements times 16); the B operand the rotated
+//                 query rows, scaled by a power of two to below 2^14 (INT4 odd elements divided by
+//                 16) and split into hi + lo fp16.  A score is s_K (q . code) + z_K sum(q).
+//   O += P' V:    the A operand is p * s_V (hi + lo fp16), the B operand the value codes (stored
+//                 dim-major) centred as fp16 integers (code - 8; INT8: - 128);
 //                 sum_t p_t (z_V,t + 8 s_V,t) is accumulated per lane.
 // Positions are assigned to the S^T rows so that the accumulator of lane l holds the scores of
 // query row l % 16 for 8 consecutive positions of the step -- exactly the positions whose p * s_V
@@ -46,11 +47,14 @@ __device__ __forceinline__ float4_t mfma16x32(u32x4 a, u32x4 b, float4_t c)
                                                   0, 0, 0);
 }
 
-// Eight INT4 codes, nibble i = element i, one per 16-bit half in the element order
-// (0, 4, 1, 5, 2, 6, 3, 7); as fp16 these are the subnormal patterns code * 2^-24 (exact).
-__device__ __forceinline__ u32x4 spread_int4(uint32_t w)
+// Eight INT4 key codes, nibble i = element i, one per 16-bit half in the element order
+// (0, 4, 1, 5, 2, 6, 3, 7); as fp16 these are the subnormal patterns code * 2^-24, the odd
+// elements multiplied by 16 (at most 240 * 2^-24, still exact): four ands and one shift.  The
+// query operand carries the 1/16 of those elements.
+__device__ __forceinline__ u32x4 spread_int4_x16(uint32_t w)
 {
-    return (u32x4){w & 0x000F000Fu, (w >> 4) & 0x000F000Fu, (w >> 8) & 0x000F000Fu, (w >> 12) & 0x000F000Fu};
+    const uint32_t w8 = w >> 8;
+    return (u32x4){w & 0x000F000Fu, w & 0x00F000F0u, w8 & 0x000F000Fu, w8 & 0x00F000F0u};
 }
 
 // Eight INT8 codes (bytes of w0 = elements 0..3, of w1 = elements 4..7), same order.
@@ -91,6 +95,21 @@ __device__ __forceinline__ u32x4 spread_centre_int4(uint32_t w, uint32_t k6400)
     for (int s = 0; s < 4; s++)
         r[s] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, ((w >> (4 * s)) & 0x000F000Fu) | k6400) + off);
     return r;
+}
+
+// A pair of fp16 values times 16 (exact: the values stay below 2^14).
+__device__ __forceinline__ uint32_t pair_x16(uint32_t v)
+{
+    const half2_t k16 = {(_Float16)16.f, (_Float16)16.f};
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, v) * k16);
+}
+
+// Query operand registers 1 and 3 (the odd elements) times 16, for key codes without that factor.
+// The elements pass through pair_x16 by value: hipcc's bit cast of a vector-element lvalue (q[1])
+// reads element 0.
+__device__ __forceinline__ u32x4 odd_x16(u32x4 q)
+{
+    return (u32x4){q[0], pair_x16(q[1]), q[2], pair_x16(q[3])};
 }
 
 // hi + lo fp16 of eight floats, same element order as the spreads.
@@ -223,15 +242,17 @@ struct MqWave {
         mx = fmaxf(mx, lane_xor16(mx));
         mx = max_xor32(mx);
         const int E = __builtin_amdgcn_frexp_expf(mx); // mx < 2^E
+        // q 2^(14-E): below 2^14, so that the fp16 hi and lo parts stay normal; the odd elements of
+        // each group of 8 are divided by 16 (their INT4 key codes arrive multiplied by 16)
 #pragma unroll
         for (int j = 0; j < KS; j++) {
             float y[8];
 #pragma unroll
-            for (int i = 0; i < 8; i++) y[i] = __builtin_ldexpf(x[8 * j + i], -E);
+            for (int i = 0; i < 8; i++) y[i] = __builtin_ldexpf(x[8 * j + i], 14 - E - ((i & 1) ? 4 : 0));
             split_hilo(y, qhi[j], qlo[j]);
         }
-        // score (log2 units) = Ar * s_K * acc + Br * z_K, acc = 2^-24 sum(q 2^-E * code)
-        Ar = __builtin_ldexpf(a.scale_log2, 24 + E);
+        // score (log2 units) = Ar * s_K * acc + Br * z_K, acc = 2^-24 sum(q 2^(14-E) * code)
+        Ar = __builtin_ldexpf(a.scale_log2, 24 + E - 14);
         Br = a.scale_log2 * sum;
 #pragma unroll
         for (int c = 0; c < NCB; c++) acc[c] = (float4_t){0.f, 0.f, 0.f, 0.f};
@@ -374,12 +395,14 @@ struct MqWave {
         float4_t sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < KS; j++) {
-            const u32x4 ka = IS8 ? spread_int8(b.k[0][2 * j], b.k[0][2 * j + 1]) : spread_int4(b.k[0][j]);
-            const u32x4 kb = IS8 ? spread_int8(b.k[1][2 * j], b.k[1][2 * j + 1]) : spread_int4(b.k[1][j]);
-            sa = mfma16x32(ka, qhi[j], sa);
-            sb = mfma16x32(kb, qhi[j], sb);
-            sa = mfma16x32(ka, qlo[j], sa);
-            sb = mfma16x32(kb, qlo[j], sb);
+            const u32x4 ka = IS8 ? spread_int8(b.k[0][2 * j], b.k[0][2 * j + 1]) : spread_int4_x16(b.k[0][j]);
+            const u32x4 kb = IS8 ? spread_int8(b.k[1][2 * j], b.k[1][2 * j + 1]) : spread_int4_x16(b.k[1][j]);
+            const u32x4 qh = IS8 ? odd_x16(qhi[j]) : qhi[j];
+            const u32x4 ql = IS8 ? odd_x16(qlo[j]) : qlo[j];
+            sa = mfma16x32(ka, qh, sa);
+            sb = mfma16x32(kb, qh, sb);
+            sa = mfma16x32(ka, ql, sa);
+            sb = mfma16x32(kb, ql, sb);
         }
         // fp16 scales enter the fp32 arithmetic as fma operands (v_fma_mix_f32: no conversions).
         // The reference bound uses one exponent per lane: the largest s_V of the lane's readable

@@ -298,3 +298,19 @@ def test_kernels_use_no_scratch(libkv4):
     for k, v in rep.items():
         if "decode_split_kernel" in k or "mq_split_kernel" in k:
             assert v["occupancy"] >= 2, (k, v)
+
+
+def test_no_bit_cast_of_vector_element_lvalue():
+    """hipcc mistranslates a bit cast whose whole argument is one element of an ext_vector
+    (`__builtin_bit_cast(half2_t, q[1])` read element 0 of q).  Device code passes such elements
+    through a function parameter or an expression instead; this keeps the pattern out."""
+    csrc = os.path.join(ROOT, "int4_kv_cache_fwht_amd", "csrc")
+    pat = re.compile(r"__builtin_bit_cast\(\s*[\w:]+\s*,\s*[\w.]+(\[[^\]\[]*\])+\s*\)")
+    bad = []
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".cuh", ".h", ".hpp")):
+            with open(os.path.join(csrc, name)) as f:
+                for i, line in enumerate(f, 1):
+                    if pat.search(line):
+                        bad.append("%s:%d: %s" % (name, i, line.strip()))
+    assert not bad, bad
