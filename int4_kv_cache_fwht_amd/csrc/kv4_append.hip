@@ -14,7 +14,10 @@ namespace kv4 {
 // append
 // ---------------------------------------------------------------------------------------------
 // One wave per (task, kv head).  Lane l handles row l/2 (rows 0..15: K of page slot 0..15,
-// rows 16..31: V of slot 0..15) and half l%2 of its D dims.
+// rows 16..31: V of slot 0..15): with Q = D/4 and h = l%2, its values are dims Q h .. Q h + Q - 1
+// and D/2 + Q h .. D/2 + Q h + Q - 1.  A rotate-half RoPE pair (i, i + D/2) then sits in one lane;
+// the butterfly stages of span < Q run inside each quarter block, span Q pairs the lanes l and
+// l ^ 1, and span D/2 pairs the lane's two quarter blocks.
 
 template <int N>
 __device__ __forceinline__ void fwht_in_lane(float (&y)[N], int b)
@@ -69,9 +72,10 @@ __device__ __forceinline__ QuantParams quant_params(float mn, float mx, float Qf
 }
 
 template <int D, int FMT>
-__global__ __launch_bounds__(64) void append_kernel(AppendArgs a)
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FMT == FMT_INT4_PROT ? 4 : 1))) void append_kernel(AppendArgs a)
 {
-    constexpr int N = D / 2;
+    constexpr int N = D / 2; // values per lane
+    constexpr int Q = D / 4; // dims per quarter block
     // V rows staged for the dim-major V layout: INT4 packed rows [16][D/2], INT8 rows [16][D],
     // bf16 rows [16][D] x 2 B
     __shared__ __align__(16) uint8_t lds[16 * D * 2];
@@ -90,26 +94,45 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a)
     const int t = tk.t0 - s0 + slot;
     if (lane == 0 && h == 0 && (tk.flags & kTaskNewPage)) a.bt[tk.bt_index] = tk.page;
     uint8_t* pb = a.pool + ((int64_t)tk.page * a.hkv + h) * a.page_block;
+    // dim of the lane's value i
+    auto dimof = [&](int i) { return i < Q ? Q * half + i : D / 2 + Q * half + (i - Q); };
 
     u32x4 raw[N / 8];
     if (active) {
-        const uint16_t* src = (is_v ? a.v : a.k) + ((int64_t)(tk.row0 + slot - s0) * a.hkv + h) * D + half * N;
+        const uint16_t* src = (is_v ? a.v : a.k) + ((int64_t)(tk.row0 + slot - s0) * a.hkv + h) * D;
 #pragma unroll
-        for (int q = 0; q < N / 8; q++) raw[q] = *(const u32x4*)(src + 8 * q);
+        for (int q = 0; q < N / 8; q++) raw[q] = *(const u32x4*)(src + dimof(8 * q));
     } else {
 #pragma unroll
         for (int q = 0; q < N / 8; q++) raw[q] = (u32x4){0u, 0u, 0u, 0u};
+    }
+    // fused RoPE: the key row's cos / sin table values for its dims Q h + j (j < Q), loaded with
+    // the rows so that their latency overlaps
+    const bool rope = FMT != FMT_BF16 && a.rope_cos != nullptr && !is_v;
+    float4_t rc[FMT != FMT_BF16 ? Q / 4 : 1], rs[FMT != FMT_BF16 ? Q / 4 : 1];
+    if constexpr (FMT != FMT_BF16) {
+        if (rope) {
+            const int tr = active ? t : 0;
+            const float* cr = a.rope_cos + (int64_t)tr * N + Q * half;
+            const float* sr = a.rope_sin + (int64_t)tr * N + Q * half;
+#pragma unroll
+            for (int q = 0; q < Q / 4; q++) {
+                rc[q] = *(const float4_t*)(cr + 4 * q);
+                rs[q] = *(const float4_t*)(sr + 4 * q);
+            }
+        }
     }
 
     if constexpr (FMT == FMT_BF16) {
         uint16_t* lds_bf = (uint16_t*)lds; // [16][D]
         if (active) {
             if (!is_v) {
+                // K: [D/8 chunks][16 slots][16 B]
 #pragma unroll
-                for (int q = 0; q < N / 8; q++) *(u32x4*)(pb + (half * (N / 8) + q) * 256 + slot * 16) = raw[q];
+                for (int q = 0; q < N / 8; q++) *(u32x4*)(pb + (dimof(8 * q) / 8) * 256 + slot * 16) = raw[q];
             } else {
 #pragma unroll
-                for (int q = 0; q < N / 8; q++) *(u32x4*)(lds_bf + slot * D + half * N + 8 * q) = raw[q];
+                for (int q = 0; q < N / 8; q++) *(u32x4*)(lds_bf + slot * D + dimof(8 * q)) = raw[q];
             }
         }
         __syncthreads();
@@ -134,36 +157,44 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a)
         return;
     } else {
         // ---- rotate ----
+        // bf16 -> fp32 by pairs of 8-value groups (q in the first quarter block, q + Q/8 in the
+        // second), each pair followed by the fused RoPE of its key values: the pair (i, i + D/2)
+        // is values j and j + Q of the lane (i = Q h + j); binary32,
+        // (x_i c - x_{i+D/2} s, x_{i+D/2} c + x_i s) with the caller's table row of t
         float y[N];
 #pragma unroll
-        for (int q = 0; q < N / 8; q++) {
+        for (int q = 0; q < Q / 8; q++) {
 #pragma unroll
-            for (int j = 0; j < 4; j++) {
-                y[8 * q + 2 * j] = as_float(raw[q][j] << 16);
-                y[8 * q + 2 * j + 1] = as_float(raw[q][j] & 0xFFFF0000u);
-            }
-        }
-        // ---- fused RoPE of key rows: the pair (i, i + D/2) is element i of the row's two halves;
-        // binary32, (x_i c - x_{i+D/2} s, x_{i+D/2} c + x_i s) with the caller's table row of t ----
-        if (a.rope_cos != nullptr && !is_v) {
-            const int tr = active ? t : 0;
-            const float* cr = a.rope_cos + (int64_t)tr * N;
-            const float* sr = a.rope_sin + (int64_t)tr * N;
-#pragma unroll
-            for (int q = 0; q < N / 4; q++) {
-                const float4_t c4 = *(const float4_t*)(cr + 4 * q);
-                const float4_t s4 = *(const float4_t*)(sr + 4 * q);
+            for (int k = 0; k < 2; k++) {
+                const int g8 = q + k * (Q / 8);
 #pragma unroll
                 for (int j = 0; j < 4; j++) {
-                    const float own = y[4 * q + j];
-                    const float other = dpp_xor1(own);
-                    const float oc = own * c4[j], os = other * s4[j];
-                    y[4 * q + j] = half ? oc + os : oc - os;
+                    y[8 * g8 + 2 * j] = as_float(raw[g8][j] << 16);
+                    y[8 * g8 + 2 * j + 1] = as_float(raw[g8][j] & 0xFFFF0000u);
+                }
+            }
+            if (rope) {
+#pragma unroll
+                for (int j = 8 * q; j < 8 * q + 8; j++) {
+                    const float c = rc[j / 4][j % 4], sn = rs[j / 4][j % 4];
+                    const float x0 = y[j], x1 = y[Q + j];
+                    y[j] = x0 * c - x1 * sn;
+                    y[Q + j] = x1 * c + x0 * sn;
                 }
             }
         }
-        fwht_in_lane<N>(y, a.block);
-        if (a.block == D) fwht_across_pair<N>(y, half);
+        // stages h = 1, 2, ..., b/2 in that order: h < Q inside each quarter block, h = Q across
+        // the lane pair, h = D/2 between the lane's two quarter blocks
+        fwht_in_lane<N>(y, a.block < Q ? a.block : Q);
+        if (a.block > Q) fwht_across_pair<N>(y, half);
+        if (a.block > D / 2) {
+#pragma unroll
+            for (int i = 0; i < Q; i++) {
+                const float a0 = y[i], c0 = y[i + Q];
+                y[i] = a0 + c0;
+                y[i + Q] = a0 - c0;
+            }
+        }
         if (a.block > 1) {
 #pragma unroll
             for (int i = 0; i < N; i++) y[i] = y[i] * a.cb;
@@ -238,17 +269,27 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a)
                 pk[q] = e | (o << 4);
             }
             if (active) {
-                if (!is_v) {
-                    // K: [D/32 chunks][16 slots][16 B]; this half covers chunks half*N/32 ..
+                // K: [D/32 chunks][16 slots][16 B]; V staged as packed rows [16][D/2]
+                if constexpr (Q >= 32) {
 #pragma unroll
-                    for (int c = 0; c < N / 32; c++)
-                        *(u32x4*)(pb + (half * (N / 32) + c) * 256 + slot * 16) =
-                            (u32x4){pk[4 * c], pk[4 * c + 1], pk[4 * c + 2], pk[4 * c + 3]};
+                    for (int c = 0; c < N / 32; c++) {
+                        const int d0 = dimof(32 * c);
+                        const u32x4 w = {pk[4 * c], pk[4 * c + 1], pk[4 * c + 2], pk[4 * c + 3]};
+                        if (!is_v)
+                            *(u32x4*)(pb + (d0 / 32) * 256 + slot * 16) = w;
+                        else
+                            *(u32x4*)(lds_v4 + slot * (D / 2) + d0 / 2) = w;
+                    }
                 } else {
 #pragma unroll
-                    for (int c = 0; c < N / 32; c++)
-                        *(u32x4*)(lds_v4 + slot * (D / 2) + half * (N / 2) + 16 * c) =
-                            (u32x4){pk[4 * c], pk[4 * c + 1], pk[4 * c + 2], pk[4 * c + 3]};
+                    for (int c = 0; c < N / 16; c++) {
+                        const int d0 = dimof(16 * c);
+                        const u32x2 w = {pk[2 * c], pk[2 * c + 1]};
+                        if (!is_v)
+                            *(u32x2*)(pb + (d0 / 32) * 256 + slot * 16 + (d0 % 32) / 2) = w;
+                        else
+                            *(u32x2*)(lds_v4 + slot * (D / 2) + d0 / 2) = w;
+                    }
                 }
                 if (half == 0)
                     *(uint32_t*)(pb + 16 * D + slot * 8 + (is_v ? 4 : 0)) = qp.s_bits | (qp.z_bits << 16);
@@ -269,22 +310,20 @@ __global__ __launch_bounds__(64) void append_kernel(AppendArgs a)
                     tb = a.int8_pool + (((int64_t)tk.seq * a.hkv + h) * a.int8_tiles + (u >> 4)) * a.int8_tile;
                     s8 = u & 15;
                 }
-                // the tile is two blocks of 16D + 128 bytes; block `half` holds K dims half*D/2 ..
-                uint8_t* bh = tb + half * (16 * D + 128);
-                if (!is_v) {
-                    // K8 of this half: [D/32 chunks][16 slots][16 B]
+                // the tile is two blocks of 16D + 128 bytes; block x holds K dims x*D/2 .. as
+                // [D/32 chunks of 16 dims][16 slots][16 B]
+                constexpr int BB = 16 * D + 128;
 #pragma unroll
-                    for (int c = 0; c < N / 16; c++)
-                        *(u32x4*)(bh + c * 256 + s8 * 16) =
-                            (u32x4){cb8[4 * c], cb8[4 * c + 1], cb8[4 * c + 2], cb8[4 * c + 3]};
-                } else {
-#pragma unroll
-                    for (int c = 0; c < N / 16; c++)
-                        *(u32x4*)(lds_v8 + slot * D + half * N + 16 * c) =
-                            (u32x4){cb8[4 * c], cb8[4 * c + 1], cb8[4 * c + 2], cb8[4 * c + 3]};
+                for (int c = 0; c < N / 16; c++) {
+                    const int d0 = dimof(16 * c);
+                    const u32x4 w = {cb8[4 * c], cb8[4 * c + 1], cb8[4 * c + 2], cb8[4 * c + 3]};
+                    if (!is_v)
+                        *(u32x4*)(tb + (d0 / (D / 2)) * BB + ((d0 % (D / 2)) / 16) * 256 + s8 * 16) = w;
+                    else
+                        *(u32x4*)(lds_v8 + slot * D + d0) = w;
                 }
-                // scales: a copy in each block
-                *(uint32_t*)(bh + 16 * D + s8 * 8 + (is_v ? 4 : 0)) = qp.s_bits | (qp.z_bits << 16);
+                // scales: a copy in each block (block `half` from this lane)
+                *(uint32_t*)(tb + half * BB + 16 * D + s8 * 8 + (is_v ? 4 : 0)) = qp.s_bits | (qp.z_bits << 16);
             }
         }
         __syncthreads();
