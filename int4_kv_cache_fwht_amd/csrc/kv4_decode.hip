@@ -943,23 +943,35 @@ __global__ __launch_bounds__(64 * G) void merge_kernel(DecodeArgs a)
     const int64_t sb = U.step_begin + kUnitStartSteps;
     const int64_t w0 = wave_of_step(sb, T, W), w1 = wave_of_step(se - 1, T, W);
     const int n = (int)(w1 - w0 + 1);
-    // partial j of this unit sits at index w0 + u + j; (m, l) are read with scalar loads (the split
-    // kernel that wrote them has completed)
+    // partial j of this unit sits at index w0 + u + j.  Lane j of a round of 64 holds partial
+    // j's (m, l): one vector load per round instead of a scalar load (and its wait) per partial.
     const float* ml = a.part_ml + ((w0 + u) * G + i) * 2;
     const float* po = a.part_o + ((w0 + u) * G + i) * D + lane;
     float M = -INFINITY;
-    for (int j = 0; j < n; j++) M = fmaxf(M, ld_uniform(ml + (int64_t)j * G * 2));
+    for (int j0 = 0; j0 < n; j0 += 64) {
+        const int j = j0 + lane;
+        M = fmaxf(M, j < n ? ml[(int64_t)j * G * 2] : -INFINITY);
+    }
+    M = wave_max_u(M);
     float Ls = 0.f, O[NHV];
 #pragma unroll
     for (int hv = 0; hv < NHV; hv++) O[hv] = 0.f;
     if (M != -INFINITY) {
-#pragma unroll 16
-        for (int j = 0; j < n; j++) {
-            const float mw = ld_uniform(ml + (int64_t)j * G * 2);
-            const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-            Ls = fmaf(ld_uniform(ml + (int64_t)j * G * 2 + 1), f, Ls);
+        for (int j0 = 0; j0 < n; j0 += 64) {
+            const int j = j0 + lane;
+            const float mj = j < n ? ml[(int64_t)j * G * 2] : -INFINITY;
+            const float lj = j < n ? ml[(int64_t)j * G * 2 + 1] : 0.f;
+            const float fj = (mj == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mj - M);
+            Ls += wave_sum_u(fj * lj);
+            // the outputs in partial order, each weight read from its lane
+            const int jn = n - j0 < 64 ? n - j0 : 64;
+#pragma unroll 8
+            for (int jj = 0; jj < jn; jj++) {
+                const float f = as_float((uint32_t)__builtin_amdgcn_readlane((int)as_uint(fj), jj));
 #pragma unroll
-            for (int hv = 0; hv < NHV; hv++) O[hv] = fmaf(po[(int64_t)j * G * D + 64 * hv], f, O[hv]);
+                for (int hv = 0; hv < NHV; hv++)
+                    O[hv] = fmaf(po[(int64_t)(j0 + jj) * G * D + 64 * hv], f, O[hv]);
+            }
         }
     }
     float r[NHV];

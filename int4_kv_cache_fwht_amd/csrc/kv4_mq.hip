@@ -144,6 +144,22 @@ __device__ __forceinline__ u32x4 ld16(const uint8_t* p) { return *(const u32x4*)
 __device__ __forceinline__ u32x2 ld8(const uint8_t* p) { return *(const u32x2*)p; }
 __device__ __forceinline__ uint32_t ld4(const uint8_t* p) { return *(const uint32_t*)p; }
 
+// The call entry that holds `key`: the last entry whose first task (GRP false) or first merge
+// group (GRP true) is <= key (both increase along the entries).  Lane l reads entry l of each round
+// of 64 and a ballot counts them: one load per round instead of a chain of dependent scalar loads.
+template <bool GRP>
+__device__ __forceinline__ int mq_find_entry(const MqArgs& a, int key, int lane)
+{
+    int cnt = 0;
+    for (int e0 = 0; e0 < a.n_entries; e0 += 64) {
+        const int e = e0 + lane;
+        const int v = e < a.n_entries ? (GRP ? a.entries[e].grp0 : a.entries[e].task0) : 0x7FFFFFFF;
+        cnt += __builtin_popcountll(__ballot(v <= key));
+        if (__ballot(v > key) != 0ull) break;
+    }
+    return cnt - 1;
+}
+
 template <typename T>
 __device__ __forceinline__ const T* pick(bool c, const T* x, const T* y)
 {
@@ -532,14 +548,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     const int wave = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
     if (wave >= a.tasks) return;
     const int lane = (int)(threadIdx.x & 63);
-    int lo = 0, hi = a.n_entries - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (mq_uniform(&a.entries[mid].task0) <= wave)
-            lo = mid;
-        else
-            hi = mid - 1;
-    }
+    const int lo = mq_find_entry<false>(a, wave, lane);
     MqEntry e;
     e.seq = mq_uniform(&a.entries[lo].seq);
     e.len = mq_uniform(&a.entries[lo].len);
@@ -593,14 +602,7 @@ __global__ __launch_bounds__(256) void mq_merge_kernel(MqArgs a)
     if (wave >= a.groups * kMqRows) return;
     const int lane = (int)(threadIdx.x & 63);
     const int grp = wave / kMqRows, r = wave % kMqRows;
-    int lo = 0, hi = a.n_entries - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (mq_uniform(&a.entries[mid].grp0) <= grp)
-            lo = mid;
-        else
-            hi = mid - 1;
-    }
+    const int lo = mq_find_entry<true>(a, grp, lane);
     const int nq = mq_uniform(&a.entries[lo].nq);
     const int qrow0 = mq_uniform(&a.entries[lo].qrow0);
     const int task0 = mq_uniform(&a.entries[lo].task0);
@@ -611,23 +613,34 @@ __global__ __launch_bounds__(256) void mq_merge_kernel(MqArgs a)
     const int head = local / nrt, rt = local - head * nrt;
     const int jq = rt * QT + r / G, gi = r % G;
     if (jq >= nq) return;
+    // chunk c's partial of this row sits in task slot T(c); lane c of a round of 64 holds its
+    // (m, l), one vector load per round
+    const int64_t T0 = (int64_t)task0 + (int64_t)head * nch * nrt + rt; // T(c) = T0 + c nrt
     float M = -__builtin_inff();
-    for (int c = 0; c < nch; c++) {
-        const int64_t T = (int64_t)task0 + ((int64_t)head * nch + c) * nrt + rt;
-        M = fmaxf(M, mq_uniform(a.part_ml + (T * kMqRows + r) * 2));
+    for (int c0 = 0; c0 < nch; c0 += 64) {
+        const int c = c0 + lane;
+        M = fmaxf(M, c < nch ? a.part_ml[((T0 + (int64_t)c * nrt) * kMqRows + r) * 2] : -__builtin_inff());
     }
+    M = wave_max_u(M);
     float l = 0.f, o[DPM];
 #pragma unroll
     for (int k = 0; k < DPM; k++) o[k] = 0.f;
-    for (int c = 0; c < nch; c++) {
-        const int64_t T = (int64_t)task0 + ((int64_t)head * nch + c) * nrt + rt;
-        const float m = mq_uniform(a.part_ml + (T * kMqRows + r) * 2);
-        const float lc = mq_uniform(a.part_ml + (T * kMqRows + r) * 2 + 1);
+    for (int c0 = 0; c0 < nch; c0 += 64) {
+        const int c = c0 + lane;
+        const float* mlc = a.part_ml + ((T0 + (int64_t)c * nrt) * kMqRows + r) * 2;
+        const float m = c < nch ? mlc[0] : -__builtin_inff();
+        const float lc = c < nch ? mlc[1] : 0.f;
         const float wgt = exp2f(m - M);
-        l = fmaf(wgt, lc, l);
-        const float* po = a.part_o + (T * kMqRows + r) * D + lane * DPM;
+        l += wave_sum_u(wgt * lc);
+        // the outputs in chunk order, each weight read from its lane
+        const int cn = nch - c0 < 64 ? nch - c0 : 64;
+#pragma unroll 8
+        for (int cc = 0; cc < cn; cc++) {
+            const float w = as_float((uint32_t)__builtin_amdgcn_readlane((int)as_uint(wgt), cc));
+            const float* po = a.part_o + ((T0 + (int64_t)(c0 + cc) * nrt) * kMqRows + r) * D + lane * DPM;
 #pragma unroll
-        for (int k = 0; k < DPM; k++) o[k] = fmaf(wgt, po[k], o[k]);
+            for (int k = 0; k < DPM; k++) o[k] = fmaf(w, po[k], o[k]);
+        }
     }
     const float inv = 1.f / l;
 #pragma unroll
