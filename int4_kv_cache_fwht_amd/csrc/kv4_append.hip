@@ -412,14 +412,17 @@ __global__ __launch_bounds__(64) void append_token_kernel(AppendArgs a)
 {
     constexpr int PL = D / 32; // dims per lane
     AppendTask tk;
+    // task e from the argument block, read in place from the kernarg segment (always present, so
+    // read before the test of n_arg: the loads do not wait for it)
+    const int e = blockIdx.x;
+    const __attribute__((address_space(4))) char* ka =
+        (const __attribute__((address_space(4))) char*)__builtin_amdgcn_kernarg_segment_ptr();
+    const int32_t pg = ((const __attribute__((address_space(4))) int32_t*)(ka + offsetof(AppendArgs, arg_page)))[e];
+    const int32_t aseq = ((const __attribute__((address_space(4))) int32_t*)(ka + offsetof(AppendArgs, arg_seq)))[e];
+    const int32_t at0 = ((const __attribute__((address_space(4))) int32_t*)(ka + offsetof(AppendArgs, arg_t0)))[e];
     if (a.n_arg > 0) {
-        // task e from the argument block (read in place from the kernarg segment)
-        const int e = blockIdx.x;
-        const __attribute__((address_space(4))) char* ka =
-            (const __attribute__((address_space(4))) char*)__builtin_amdgcn_kernarg_segment_ptr();
-        const int32_t pg = ((const __attribute__((address_space(4))) int32_t*)(ka + offsetof(AppendArgs, arg_page)))[e];
-        tk.seq = ((const __attribute__((address_space(4))) int32_t*)(ka + offsetof(AppendArgs, arg_seq)))[e];
-        tk.t0 = ((const __attribute__((address_space(4))) int32_t*)(ka + offsetof(AppendArgs, arg_t0)))[e];
+        tk.seq = aseq;
+        tk.t0 = at0;
         tk.page = pg & 0x7FFFFFFF;
         tk.flags = pg < 0 ? kTaskNewPage : 0;
         tk.n = 1;
@@ -447,19 +450,30 @@ __global__ __launch_bounds__(64) void append_token_kernel(AppendArgs a)
     uint8_t old[PL];
 #pragma unroll
     for (int j = 0; j < PL; j++) old[j] = vbyte[8 * j];
+    // fused RoPE table values of the lane's dims (lanes l and l ^ 16 hold the pairs (i, i + D/2)),
+    // loaded with the row
+    const bool rope = a.rope_cos != nullptr;
+    float rcv[PL], rsv[PL];
+    if (rope) {
+        const float* cr = a.rope_cos + (int64_t)tk.t0 * (D / 2) + PL * (l32 & 15);
+        const float* sr = a.rope_sin + (int64_t)tk.t0 * (D / 2) + PL * (l32 & 15);
+#pragma unroll
+        for (int j = 0; j < PL; j++) {
+            rcv[j] = cr[j];
+            rsv[j] = sr[j];
+        }
+    }
 
     float y[PL];
 #pragma unroll
     for (int j = 0; j < PL; j++) y[j] = as_float((uint32_t)raw[j] << 16);
     // fused RoPE of the key row: lanes l and l ^ 16 hold the pairs (i, i + D/2)
-    if (a.rope_cos != nullptr) {
-        const float* cr = a.rope_cos + (int64_t)tk.t0 * (D / 2) + PL * (l32 & 15);
-        const float* sr = a.rope_sin + (int64_t)tk.t0 * (D / 2) + PL * (l32 & 15);
+    if (rope) {
 #pragma unroll
         for (int j = 0; j < PL; j++) {
             const float own = y[j];
             const float other = lane_xor16(own);
-            const float oc = own * cr[j], os = other * sr[j];
+            const float oc = own * rcv[j], os = other * rsv[j];
             const float r = (l32 & 16) ? oc + os : oc - os;
             y[j] = row == 0 ? r : own;
         }
