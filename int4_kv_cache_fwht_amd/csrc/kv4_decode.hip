@@ -963,14 +963,24 @@ __global__ __launch_bounds__(64 * G) void merge_kernel(DecodeArgs a)
             const float lj = j < n ? ml[(int64_t)j * G * 2 + 1] : 0.f;
             const float fj = (mj == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mj - M);
             Ls += wave_sum_u(fj * lj);
-            // the outputs in partial order, each weight read from its lane
-            const int jn = n - j0 < 64 ? n - j0 : 64;
-#pragma unroll 8
-            for (int jj = 0; jj < jn; jj++) {
-                const float f = as_float((uint32_t)__builtin_amdgcn_readlane((int)as_uint(fj), jj));
+            // the outputs in partial order, each weight read from its lane; the loads of 16
+            // partials are issued before the first of them is used
+            const int jn = __builtin_amdgcn_readfirstlane(n - j0 < 64 ? n - j0 : 64);
+            for (int jb = 0; jb < jn; jb += 16) {
+                float pv[16][NHV];
 #pragma unroll
-                for (int hv = 0; hv < NHV; hv++)
-                    O[hv] = fmaf(po[(int64_t)(j0 + jj) * G * D + 64 * hv], f, O[hv]);
+                for (int k = 0; k < 16; k++)
+#pragma unroll
+                    for (int hv = 0; hv < NHV; hv++)
+                        pv[k][hv] = jb + k < jn ? po[(int64_t)(j0 + jb + k) * G * D + 64 * hv] : 0.f;
+#pragma unroll
+                for (int k = 0; k < 16; k++) {
+                    if (jb + k < jn) {
+                        const float f = as_float((uint32_t)__builtin_amdgcn_readlane((int)as_uint(fj), jb + k));
+#pragma unroll
+                        for (int hv = 0; hv < NHV; hv++) O[hv] = fmaf(pv[k][hv], f, O[hv]);
+                    }
+                }
             }
         }
     }

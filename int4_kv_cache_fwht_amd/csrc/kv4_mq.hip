@@ -632,14 +632,28 @@ __global__ __launch_bounds__(256) void mq_merge_kernel(MqArgs a)
         const float lc = c < nch ? mlc[1] : 0.f;
         const float wgt = exp2f(m - M);
         l += wave_sum_u(wgt * lc);
-        // the outputs in chunk order, each weight read from its lane
-        const int cn = nch - c0 < 64 ? nch - c0 : 64;
-#pragma unroll 8
-        for (int cc = 0; cc < cn; cc++) {
-            const float w = as_float((uint32_t)__builtin_amdgcn_readlane((int)as_uint(wgt), cc));
-            const float* po = a.part_o + ((T0 + (int64_t)(c0 + cc) * nrt) * kMqRows + r) * D + lane * DPM;
+        // the outputs in chunk order, each weight read from its lane; the loads of 8 chunks are
+        // issued before the first of them is used (8 keeps 8 waves per SIMD)
+        const int cn = __builtin_amdgcn_readfirstlane(nch - c0 < 64 ? nch - c0 : 64);
+        // chunk c's outputs: a wave-uniform base plus the lane's offset
+        const float* obase = a.part_o + (T0 * kMqRows + r) * D;
+        const int64_t ostride = (int64_t)nrt * kMqRows * D;
+        for (int cb = 0; cb < cn; cb += 8) {
+            float pv[8][DPM];
 #pragma unroll
-            for (int k = 0; k < DPM; k++) o[k] = fmaf(w, po[k], o[k]);
+            for (int k = 0; k < 8; k++) {
+                const float* po = obase + (int64_t)(c0 + cb + k) * ostride;
+#pragma unroll
+                for (int q = 0; q < DPM; q++) pv[k][q] = cb + k < cn ? po[lane * DPM + q] : 0.f;
+            }
+#pragma unroll
+            for (int k = 0; k < 8; k++) {
+                if (cb + k < cn) {
+                    const float w = as_float((uint32_t)__builtin_amdgcn_readlane((int)as_uint(wgt), cb + k));
+#pragma unroll
+                    for (int q = 0; q < DPM; q++) o[q] = fmaf(w, pv[k][q], o[q]);
+                }
+            }
         }
     }
     const float inv = 1.f / l;
