@@ -599,30 +599,22 @@ __global__ __launch_bounds__(64) void append_token_kernel(AppendArgs a)
     }
 }
 
-hipError_t launch_append_token(int d, int n_tasks, const AppendArgs& a, hipStream_t stream)
+hipError_t launch_append_token(int d, int n_tasks, const AppendArgs& a, hipStream_t stream, const KernelTimer& tm)
 {
     if (n_tasks <= 0) return hipSuccess;
     dim3 grid((unsigned)n_tasks, (unsigned)a.hkv), block(64);
-    if (d == 64) {
-        hipLaunchKernelGGL((append_token_kernel<64>), grid, block, 0, stream, a);
-        return hipGetLastError();
-    }
-    if (d == 128) {
-        hipLaunchKernelGGL((append_token_kernel<128>), grid, block, 0, stream, a);
-        return hipGetLastError();
-    }
+    if (d == 64) return launch_kernel(append_token_kernel<64>, grid, block, stream, tm, a);
+    if (d == 128) return launch_kernel(append_token_kernel<128>, grid, block, stream, tm, a);
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_append(int d, int format, int n_tasks, const AppendArgs& a, hipStream_t stream)
+hipError_t launch_append(int d, int format, int n_tasks, const AppendArgs& a, hipStream_t stream,
+                         const KernelTimer& tm)
 {
     if (n_tasks <= 0) return hipSuccess;
     dim3 grid((unsigned)n_tasks, (unsigned)a.hkv), block(64);
-#define KV4_APPEND_CASE(DD, FF)                                                          \
-    if (d == DD && format == FF) {                                                       \
-        hipLaunchKernelGGL((append_kernel<DD, FF>), grid, block, 0, stream, a);          \
-        return hipGetLastError();                                                        \
-    }
+#define KV4_APPEND_CASE(DD, FF) \
+    if (d == DD && format == FF) return launch_kernel(append_kernel<DD, FF>, grid, block, stream, tm, a);
     KV4_APPEND_CASE(64, 0)
     KV4_APPEND_CASE(64, 1)
     KV4_APPEND_CASE(64, 2)

@@ -1,6 +1,7 @@
 // kv4_common.cuh -- device helpers shared by the libkv4 kernels (gfx950, wave64).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -20,6 +21,19 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 enum { FMT_INT4_PROT = 0, FMT_INT8 = 1, FMT_BF16 = 2 };
+
+// One launch of `kernel` with its argument struct; the timer's events, when set, are stamped from
+// the launch's own dispatch.
+template <typename Arg>
+inline hipError_t launch_kernel(void (*kernel)(Arg), dim3 grid, dim3 block, hipStream_t stream,
+                                const KernelTimer& tm, const Arg& a)
+{
+    if (tm.start || tm.stop)
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, tm.start, tm.stop, 0, a);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, 0, stream, a);
+    return hipGetLastError();
+}
 
 // ---------------------------------------------------------------------------------------------
 // small helpers

@@ -209,6 +209,14 @@ struct DecodeWave {
     const int n8;        // INT8 steps at the start of an INT4_PROT unit
 
     EntryRegs er; // argument plan (a.n_arg > 0)
+    // Issue-priority feedback between the two waves that share a SIMD (both in this workgroup).
+    // The arbiter favours the older wave, which with equal work would finish well before the
+    // younger one and leave the younger to run its last steps alone. Each wave publishes its step
+    // count in LDS (prog[own]) and takes the higher priority while it is not ahead of
+    // prog[partner]; own == partner (no partner) keeps it at the higher one.
+    int* prog = nullptr;
+    int own = 0, partner = 0;
+    int done = 0;
     half4_t A4[NPAIR], A8[NPAIR];
     short4_t Abf[NPAIR_BF];
     float4_t acc[NHV][2]; // two accumulation chains per output half
@@ -411,9 +419,16 @@ struct DecodeWave {
 #pragma unroll
             for (int i = 0; i < 4; i++) L32[(st_w * 4 + i) * 4 + kk] = pt[i];
         }
+        done++;
+        if (lane == 0) __hip_atomic_store(prog + own, done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         wave_lds_sync();
         float4_t v = *(const float4_t*)(L32 + lane * 4);
+        const int other = __hip_atomic_load(prog + partner, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         wave_lds_sync();
+        if (done <= __builtin_amdgcn_readfirstlane(other))
+            __builtin_amdgcn_s_setprio(1);
+        else
+            __builtin_amdgcn_s_setprio(0);
         if (odd16) {
             v.z *= 0.0625f;
             v.w *= 0.0625f;
@@ -877,8 +892,21 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) __attribute__((amdgpu_waves_pe
 void decode_split_kernel(DecodeArgs a)
 {
     __shared__ __align__(16) uint8_t lds_all[kWavesPerBlock][kLdsPerWave];
+    __shared__ int lds_simd[kWavesPerBlock], lds_prog[kWavesPerBlock];
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // SIMD of this wave (HW_ID bits 5:4); the partner is the other wave of the workgroup on it
+    const int simd = __builtin_amdgcn_readfirstlane(((int)__builtin_amdgcn_s_getreg((31 << 11) | 4) >> 4) & 3);
+    if (lane == 0) {
+        lds_simd[wv] = simd;
+        lds_prog[wv] = 0;
+    }
+    __syncthreads();
+    int partner = wv;
+#pragma unroll
+    for (int i = kWavesPerBlock - 1; i >= 0; i--)
+        if (i != wv && lds_simd[i] == simd) partner = i;
+    partner = __builtin_amdgcn_readfirstlane(partner);
     const int64_t w = (int64_t)blockIdx.x * kWavesPerBlock + wv;
     if (w >= a.n_waves) return;
     const int64_t T = a.total_steps, W = a.n_waves;
@@ -886,6 +914,9 @@ void decode_split_kernel(DecodeArgs a)
     const int64_t s_end = (w + 1) * T / W;
     if (s >= s_end) return;
     DecodeWave<D, G, FMT> dw(a, lane, lds_all[wv], lds_all[wv] + kLdsQBytes, w, s_end);
+    dw.prog = lds_prog;
+    dw.own = wv;
+    dw.partner = partner;
     int lo = 0;
     if (a.n_arg > 0) {
         dw.er = load_entries(a, lane);
@@ -1028,50 +1059,48 @@ __global__ __launch_bounds__(64 * G) void merge_kernel(DecodeArgs a)
 // ---------------------------------------------------------------------------------------------
 
 template <int D, int G, int F>
-static hipError_t launch_split_t(const DecodeArgs& a, hipStream_t stream)
+static hipError_t launch_split_t(const DecodeArgs& a, hipStream_t stream, const KernelTimer& tm)
 {
     const unsigned blocks = (unsigned)((a.n_waves + kWavesPerBlock - 1) / kWavesPerBlock);
-    hipLaunchKernelGGL((decode_split_kernel<D, G, F>), dim3(blocks), dim3(64 * kWavesPerBlock), 0, stream, a);
-    return hipGetLastError();
+    return launch_kernel(decode_split_kernel<D, G, F>, dim3(blocks), dim3(64 * kWavesPerBlock), stream, tm, a);
 }
 
 template <int D, int G, int F>
-static hipError_t launch_merge_t(const DecodeArgs& a, hipStream_t stream)
+static hipError_t launch_merge_t(const DecodeArgs& a, hipStream_t stream, const KernelTimer& tm)
 {
-    hipLaunchKernelGGL((merge_kernel<D, G, F>), dim3((unsigned)a.n_units), dim3(64 * G), 0, stream, a);
-    return hipGetLastError();
+    return launch_kernel(merge_kernel<D, G, F>, dim3((unsigned)a.n_units), dim3(64 * G), stream, tm, a);
 }
 
 template <int D, int G, int F>
-static hipError_t launch_merge16_t(const DecodeArgs& a, hipStream_t stream)
+static hipError_t launch_merge16_t(const DecodeArgs& a, hipStream_t stream, const KernelTimer& tm)
 {
-    hipLaunchKernelGGL((merge_kernel<D, G, F, true>), dim3((unsigned)a.n_units), dim3(64 * G), 0, stream, a);
-    return hipGetLastError();
+    return launch_kernel(merge_kernel<D, G, F, true>, dim3((unsigned)a.n_units), dim3(64 * G), stream, tm, a);
 }
 
 #define KV4_DEC_DISPATCH(FN)                                                                        \
     if (a.n_units <= 0) return hipSuccess;                                                          \
-    if (d == 64 && g == 1 && format == 0) return FN<64, 1, 0>(a, stream);                           \
-    if (d == 64 && g == 2 && format == 0) return FN<64, 2, 0>(a, stream);                           \
-    if (d == 64 && g == 4 && format == 0) return FN<64, 4, 0>(a, stream);                           \
-    if (d == 64 && g == 1 && format == 1) return FN<64, 1, 1>(a, stream);                           \
-    if (d == 64 && g == 2 && format == 1) return FN<64, 2, 1>(a, stream);                           \
-    if (d == 64 && g == 4 && format == 1) return FN<64, 4, 1>(a, stream);                           \
-    if (d == 64 && g == 1 && format == 2) return FN<64, 1, 2>(a, stream);                           \
-    if (d == 64 && g == 2 && format == 2) return FN<64, 2, 2>(a, stream);                           \
-    if (d == 64 && g == 4 && format == 2) return FN<64, 4, 2>(a, stream);                           \
-    if (d == 128 && g == 1 && format == 0) return FN<128, 1, 0>(a, stream);                         \
-    if (d == 128 && g == 2 && format == 0) return FN<128, 2, 0>(a, stream);                         \
-    if (d == 128 && g == 4 && format == 0) return FN<128, 4, 0>(a, stream);                         \
-    if (d == 128 && g == 1 && format == 1) return FN<128, 1, 1>(a, stream);                         \
-    if (d == 128 && g == 2 && format == 1) return FN<128, 2, 1>(a, stream);                         \
-    if (d == 128 && g == 4 && format == 1) return FN<128, 4, 1>(a, stream);                         \
-    if (d == 128 && g == 1 && format == 2) return FN<128, 1, 2>(a, stream);                         \
-    if (d == 128 && g == 2 && format == 2) return FN<128, 2, 2>(a, stream);                         \
-    if (d == 128 && g == 4 && format == 2) return FN<128, 4, 2>(a, stream);                         \
+    if (d == 64 && g == 1 && format == 0) return FN<64, 1, 0>(a, stream, tm);                       \
+    if (d == 64 && g == 2 && format == 0) return FN<64, 2, 0>(a, stream, tm);                       \
+    if (d == 64 && g == 4 && format == 0) return FN<64, 4, 0>(a, stream, tm);                       \
+    if (d == 64 && g == 1 && format == 1) return FN<64, 1, 1>(a, stream, tm);                       \
+    if (d == 64 && g == 2 && format == 1) return FN<64, 2, 1>(a, stream, tm);                       \
+    if (d == 64 && g == 4 && format == 1) return FN<64, 4, 1>(a, stream, tm);                       \
+    if (d == 64 && g == 1 && format == 2) return FN<64, 1, 2>(a, stream, tm);                       \
+    if (d == 64 && g == 2 && format == 2) return FN<64, 2, 2>(a, stream, tm);                       \
+    if (d == 64 && g == 4 && format == 2) return FN<64, 4, 2>(a, stream, tm);                       \
+    if (d == 128 && g == 1 && format == 0) return FN<128, 1, 0>(a, stream, tm);                     \
+    if (d == 128 && g == 2 && format == 0) return FN<128, 2, 0>(a, stream, tm);                     \
+    if (d == 128 && g == 4 && format == 0) return FN<128, 4, 0>(a, stream, tm);                     \
+    if (d == 128 && g == 1 && format == 1) return FN<128, 1, 1>(a, stream, tm);                     \
+    if (d == 128 && g == 2 && format == 1) return FN<128, 2, 1>(a, stream, tm);                     \
+    if (d == 128 && g == 4 && format == 1) return FN<128, 4, 1>(a, stream, tm);                     \
+    if (d == 128 && g == 1 && format == 2) return FN<128, 1, 2>(a, stream, tm);                     \
+    if (d == 128 && g == 2 && format == 2) return FN<128, 2, 2>(a, stream, tm);                     \
+    if (d == 128 && g == 4 && format == 2) return FN<128, 4, 2>(a, stream, tm);                     \
     return hipErrorInvalidValue;
 
-hipError_t launch_decode_split(int d, int g, int format, const DecodeArgs& a, hipStream_t stream)
+hipError_t launch_decode_split(int d, int g, int format, const DecodeArgs& a, hipStream_t stream,
+                               const KernelTimer& tm)
 {
     KV4_DEC_DISPATCH(launch_split_t)
 }
@@ -1097,12 +1126,14 @@ hipError_t decode_split_residency(int d, int g, int format, int* blocks_per_cu)
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_decode_merge(int d, int g, int format, const DecodeArgs& a, hipStream_t stream)
+hipError_t launch_decode_merge(int d, int g, int format, const DecodeArgs& a, hipStream_t stream,
+                               const KernelTimer& tm)
 {
     KV4_DEC_DISPATCH(launch_merge_t)
 }
 
-hipError_t launch_decode_merge_bf16(int d, int g, int format, const DecodeArgs& a, hipStream_t stream)
+hipError_t launch_decode_merge_bf16(int d, int g, int format, const DecodeArgs& a, hipStream_t stream,
+                                    const KernelTimer& tm)
 {
     KV4_DEC_DISPATCH(launch_merge16_t)
 }

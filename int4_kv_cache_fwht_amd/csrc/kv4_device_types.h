@@ -9,7 +9,7 @@ constexpr int kPageSize = 16;       // positions per page (one 16-slot tile per 
 constexpr int kInt4StepPages = 4;   // decode INT4 step: 4 pages = 64 positions, one per lane
 constexpr int kInt8StepSlots = 32;  // decode INT8 step over protection slots: 2 tiles = 32 slots
 constexpr int kInt8StepPages = 2;   // decode step of the INT8 format: 2 pages = 32 positions
-constexpr int kWavesPerBlock = 4;   // decode split kernel: independent waves per workgroup
+constexpr int kWavesPerBlock = 8;   // decode split kernel: waves per workgroup (two per SIMD)
 constexpr int kArgEntries = 256;    // calls with up to this many sequences pass their plan as kernel arguments
 // Decode split: every unit's step range opens with this many accounting steps that hold no work.
 // A wave whose slice starts a unit pays its query prologue, its epilogue and a refill of the load

@@ -82,13 +82,13 @@ struct Staging {
 // Event pairs / triples recorded around kernel launches while profiling is on.
 struct Profiler {
     bool on = false;
-    std::vector<std::vector<hipEvent_t>> append_ev; // {before, after}
-    std::vector<std::vector<hipEvent_t>> decode_ev; // {before split, after split, after merge}
+    std::vector<std::vector<hipEvent_t>> append_ev; // {kernel start, kernel stop}
+    std::vector<std::vector<hipEvent_t>> decode_ev; // {split start, split stop, merge start, merge stop}
     std::vector<std::vector<hipEvent_t>> mq_ev;     // the same for multi-query calls
     kv4_profile totals{};
 
-    // Timing-only events: no system-scope fence when they are recorded, so the measured interval
-    // holds the kernel and its dispatch, not a writeback of the caches to the host's view.
+    // Timing-only events (no system-scope fence). Each launch stamps its own start/stop pair from
+    // its dispatch, so an interval is one kernel's execution, as a kernel trace reports it.
     static hipError_t make(int n, std::vector<hipEvent_t>* out)
     {
         out->assign((size_t)n, nullptr);
@@ -127,11 +127,11 @@ struct Profiler {
         }
         append_ev.clear();
         for (auto& v : decode_ev) {
-            hipError_t r = hipEventSynchronize(v[2]);
+            hipError_t r = hipEventSynchronize(v[3]);
             if (r != hipSuccess) return r;
             float a = 0.f, b = 0.f;
             hipEventElapsedTime(&a, v[0], v[1]);
-            hipEventElapsedTime(&b, v[1], v[2]);
+            hipEventElapsedTime(&b, v[2], v[3]);
             totals.decode_launches += 1;
             totals.split_ms += a;
             totals.merge_ms += b;
@@ -139,11 +139,11 @@ struct Profiler {
         }
         decode_ev.clear();
         for (auto& v : mq_ev) {
-            hipError_t r = hipEventSynchronize(v[2]);
+            hipError_t r = hipEventSynchronize(v[3]);
             if (r != hipSuccess) return r;
             float a = 0.f, b = 0.f;
             hipEventElapsedTime(&a, v[0], v[1]);
-            hipEventElapsedTime(&b, v[1], v[2]);
+            hipEventElapsedTime(&b, v[2], v[3]);
             totals.mq_launches += 1;
             totals.mq_split_ms += a;
             totals.mq_merge_ms += b;
@@ -476,21 +476,18 @@ kv4_status append_impl(kv4_cache_t h, int32_t n_seqs, const int32_t* seq_ids, co
     a.rope_cos = rope_cos;
     a.rope_sin = rope_sin;
     std::vector<hipEvent_t> ev;
+    kv4::KernelTimer tm;
     if (h->prof.on) {
         e = Profiler::make(2, &ev);
-        if (e == hipSuccess) e = hipEventRecord(ev[0], strm);
         if (e != hipSuccess) return hip_fail(h, e, "profiling event");
+        tm = kv4::KernelTimer{ev[0], ev[1]};
     }
     if (single)
-        e = kv4::launch_append_token(h->st.cfg.d, (int)tasks.size(), a, strm);
+        e = kv4::launch_append_token(h->st.cfg.d, (int)tasks.size(), a, strm, tm);
     else
-        e = kv4::launch_append(h->st.cfg.d, h->st.cfg.format, (int)tasks.size(), a, strm);
+        e = kv4::launch_append(h->st.cfg.d, h->st.cfg.format, (int)tasks.size(), a, strm, tm);
     if (e != hipSuccess) return hip_fail(h, e, "append launch");
-    if (h->prof.on) {
-        e = hipEventRecord(ev[1], strm);
-        if (e != hipSuccess) return hip_fail(h, e, "profiling event");
-        h->prof.append_ev.push_back(ev);
-    }
+    if (h->prof.on) h->prof.append_ev.push_back(ev);
     return KV4_OK;
 }
 
@@ -611,25 +608,19 @@ kv4_status decode_impl(kv4_cache_t h, int32_t n_seqs, const int32_t* seq_ids, co
         }
     }
     std::vector<hipEvent_t> ev;
+    kv4::KernelTimer t_split, t_merge;
     if (h->prof.on) {
-        e = Profiler::make(3, &ev);
-        if (e == hipSuccess) e = hipEventRecord(ev[0], strm);
+        e = Profiler::make(4, &ev);
         if (e != hipSuccess) return hip_fail(h, e, "profiling event");
+        t_split = kv4::KernelTimer{ev[0], ev[1]};
+        t_merge = kv4::KernelTimer{ev[2], ev[3]};
     }
-    e = kv4::launch_decode_split(D, G, h->st.cfg.format, a, strm);
+    e = kv4::launch_decode_split(D, G, h->st.cfg.format, a, strm, t_split);
     if (e != hipSuccess) return hip_fail(h, e, "decode split launch");
-    if (h->prof.on) {
-        e = hipEventRecord(ev[1], strm);
-        if (e != hipSuccess) return hip_fail(h, e, "profiling event");
-    }
-    e = out16 ? kv4::launch_decode_merge_bf16(D, G, h->st.cfg.format, a, strm)
-              : kv4::launch_decode_merge(D, G, h->st.cfg.format, a, strm);
+    e = out16 ? kv4::launch_decode_merge_bf16(D, G, h->st.cfg.format, a, strm, t_merge)
+              : kv4::launch_decode_merge(D, G, h->st.cfg.format, a, strm, t_merge);
     if (e != hipSuccess) return hip_fail(h, e, "decode merge launch");
-    if (h->prof.on) {
-        e = hipEventRecord(ev[2], strm);
-        if (e != hipSuccess) return hip_fail(h, e, "profiling event");
-        h->prof.decode_ev.push_back(ev);
-    }
+    if (h->prof.on) h->prof.decode_ev.push_back(ev);
     return KV4_OK;
 }
 
@@ -721,24 +712,18 @@ kv4_status kv4_multi_query_attention(kv4_cache_t h, int32_t n_seqs, const int32_
     const double sc = scale > 0.f ? (double)scale : 1.0 / std::sqrt((double)D);
     a.scale_log2 = (float)(sc * 1.4426950408889634);
     std::vector<hipEvent_t> ev;
+    kv4::KernelTimer t_split, t_merge;
     if (h->prof.on) {
-        e = Profiler::make(3, &ev);
-        if (e == hipSuccess) e = hipEventRecord(ev[0], strm);
+        e = Profiler::make(4, &ev);
         if (e != hipSuccess) return hip_fail(h, e, "profiling event");
+        t_split = kv4::KernelTimer{ev[0], ev[1]};
+        t_merge = kv4::KernelTimer{ev[2], ev[3]};
     }
-    e = kv4::launch_mq_split(D, G, h->st.cfg.format, a, strm);
+    e = kv4::launch_mq_split(D, G, h->st.cfg.format, a, strm, t_split);
     if (e != hipSuccess) return hip_fail(h, e, "multi-query split launch");
-    if (h->prof.on) {
-        e = hipEventRecord(ev[1], strm);
-        if (e != hipSuccess) return hip_fail(h, e, "profiling event");
-    }
-    e = kv4::launch_mq_merge(D, G, a, strm);
+    e = kv4::launch_mq_merge(D, G, a, strm, t_merge);
     if (e != hipSuccess) return hip_fail(h, e, "multi-query merge launch");
-    if (h->prof.on) {
-        e = hipEventRecord(ev[2], strm);
-        if (e != hipSuccess) return hip_fail(h, e, "profiling event");
-        h->prof.mq_ev.push_back(ev);
-    }
+    if (h->prof.on) h->prof.mq_ev.push_back(ev);
     return KV4_OK;
 }
 

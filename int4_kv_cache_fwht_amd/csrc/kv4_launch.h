@@ -9,6 +9,14 @@
 
 namespace kv4 {
 
+// Optional timing events of one launch. When set, the launch stamps them from its own dispatch
+// (hipExtLaunchKernel), so their interval is the kernel's execution alone; unset, the launch is a
+// plain one.
+struct KernelTimer {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+
 struct AppendArgs {
     const AppendTask* tasks; // device copy of the call's tasks
     const uint16_t* k;       // bf16 [rows][hkv][D]
@@ -76,19 +84,25 @@ struct MqArgs {
     float scale_log2; // softmax scale * log2(e)
 };
 
-hipError_t launch_append(int d, int format, int n_tasks, const AppendArgs& a, hipStream_t stream);
+hipError_t launch_append(int d, int format, int n_tasks, const AppendArgs& a, hipStream_t stream,
+                         const KernelTimer& tm = KernelTimer{});
 // INT4_PROT append where every task writes exactly one position.
-hipError_t launch_append_token(int d, int n_tasks, const AppendArgs& a, hipStream_t stream);
-hipError_t launch_decode_split(int d, int g, int format, const DecodeArgs& a, hipStream_t stream);
-hipError_t launch_decode_merge(int d, int g, int format, const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_append_token(int d, int n_tasks, const AppendArgs& a, hipStream_t stream,
+                               const KernelTimer& tm = KernelTimer{});
+hipError_t launch_decode_split(int d, int g, int format, const DecodeArgs& a, hipStream_t stream,
+                               const KernelTimer& tm = KernelTimer{});
+hipError_t launch_decode_merge(int d, int g, int format, const DecodeArgs& a, hipStream_t stream,
+                               const KernelTimer& tm = KernelTimer{});
 // The same merge writing bf16 output rows (a.out then points at bf16 [entries][hq][D]).
-hipError_t launch_decode_merge_bf16(int d, int g, int format, const DecodeArgs& a, hipStream_t stream);
-// Workgroups of the split kernel (4 waves each) that fit on one compute unit at once.
+hipError_t launch_decode_merge_bf16(int d, int g, int format, const DecodeArgs& a, hipStream_t stream,
+                                    const KernelTimer& tm = KernelTimer{});
+// Workgroups of the split kernel (kWavesPerBlock waves each) that fit on one compute unit at once.
 hipError_t decode_split_residency(int d, int g, int format, int* blocks_per_cu);
 // Multi-query attention (INT4_PROT and INT8 formats): split kernel over the call's wave tasks,
 // then the merge that also applies the inverse rotation.
-hipError_t launch_mq_split(int d, int g, int format, const MqArgs& a, hipStream_t stream);
-hipError_t launch_mq_merge(int d, int g, const MqArgs& a, hipStream_t stream);
+hipError_t launch_mq_split(int d, int g, int format, const MqArgs& a, hipStream_t stream,
+                           const KernelTimer& tm = KernelTimer{});
+hipError_t launch_mq_merge(int d, int g, const MqArgs& a, hipStream_t stream, const KernelTimer& tm = KernelTimer{});
 hipError_t mq_split_residency(int d, int g, int format, int* blocks_per_cu);
 
 } // namespace kv4

@@ -686,20 +686,18 @@ __global__ __launch_bounds__(256) void mq_merge_kernel(MqArgs a)
 }
 
 template <int D, int G, int FMT>
-hipError_t split_dispatch(const MqArgs& a, hipStream_t stream)
+hipError_t split_dispatch(const MqArgs& a, hipStream_t stream, const KernelTimer& tm)
 {
     const int blocks = (a.tasks + 3) / 4;
-    hipLaunchKernelGGL((mq_split_kernel<D, G, FMT>), dim3(blocks), dim3(256), 0, stream, a);
-    return hipGetLastError();
+    return launch_kernel(mq_split_kernel<D, G, FMT>, dim3(blocks), dim3(256), stream, tm, a);
 }
 
 template <int D, int G>
-hipError_t merge_dispatch(const MqArgs& a, hipStream_t stream)
+hipError_t merge_dispatch(const MqArgs& a, hipStream_t stream, const KernelTimer& tm)
 {
     const int64_t waves = (int64_t)a.groups * kMqRows;
     const int blocks = (int)((waves + 3) / 4);
-    hipLaunchKernelGGL((mq_merge_kernel<D, G, true>), dim3(blocks), dim3(256), 0, stream, a);
-    return hipGetLastError();
+    return launch_kernel(mq_merge_kernel<D, G, true>, dim3(blocks), dim3(256), stream, tm, a);
 }
 
 template <int D, int G, int FMT>
@@ -711,14 +709,14 @@ hipError_t split_residency(int* bpc)
 } // namespace
 
 template <int FMT>
-hipError_t split_by_shape(int d, int g, const MqArgs& a, hipStream_t st)
+hipError_t split_by_shape(int d, int g, const MqArgs& a, hipStream_t st, const KernelTimer& tm)
 {
-    if (d == 128 && g == 4) return split_dispatch<128, 4, FMT>(a, st);
-    if (d == 128 && g == 2) return split_dispatch<128, 2, FMT>(a, st);
-    if (d == 128 && g == 1) return split_dispatch<128, 1, FMT>(a, st);
-    if (d == 64 && g == 4) return split_dispatch<64, 4, FMT>(a, st);
-    if (d == 64 && g == 2) return split_dispatch<64, 2, FMT>(a, st);
-    if (d == 64 && g == 1) return split_dispatch<64, 1, FMT>(a, st);
+    if (d == 128 && g == 4) return split_dispatch<128, 4, FMT>(a, st, tm);
+    if (d == 128 && g == 2) return split_dispatch<128, 2, FMT>(a, st, tm);
+    if (d == 128 && g == 1) return split_dispatch<128, 1, FMT>(a, st, tm);
+    if (d == 64 && g == 4) return split_dispatch<64, 4, FMT>(a, st, tm);
+    if (d == 64 && g == 2) return split_dispatch<64, 2, FMT>(a, st, tm);
+    if (d == 64 && g == 1) return split_dispatch<64, 1, FMT>(a, st, tm);
     return hipErrorInvalidValue;
 }
 
@@ -734,23 +732,23 @@ hipError_t residency_by_shape(int d, int g, int* bpc)
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_mq_split(int d, int g, int format, const MqArgs& a, hipStream_t stream)
+hipError_t launch_mq_split(int d, int g, int format, const MqArgs& a, hipStream_t stream, const KernelTimer& tm)
 {
     if (a.tasks <= 0) return hipSuccess;
-    if (format == FMT_INT4_PROT) return split_by_shape<FMT_INT4_PROT>(d, g, a, stream);
-    if (format == FMT_INT8) return split_by_shape<FMT_INT8>(d, g, a, stream);
+    if (format == FMT_INT4_PROT) return split_by_shape<FMT_INT4_PROT>(d, g, a, stream, tm);
+    if (format == FMT_INT8) return split_by_shape<FMT_INT8>(d, g, a, stream, tm);
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_mq_merge(int d, int g, const MqArgs& a, hipStream_t stream)
+hipError_t launch_mq_merge(int d, int g, const MqArgs& a, hipStream_t stream, const KernelTimer& tm)
 {
     if (a.groups <= 0) return hipSuccess;
-    if (d == 128 && g == 4) return merge_dispatch<128, 4>(a, stream);
-    if (d == 128 && g == 2) return merge_dispatch<128, 2>(a, stream);
-    if (d == 128 && g == 1) return merge_dispatch<128, 1>(a, stream);
-    if (d == 64 && g == 4) return merge_dispatch<64, 4>(a, stream);
-    if (d == 64 && g == 2) return merge_dispatch<64, 2>(a, stream);
-    if (d == 64 && g == 1) return merge_dispatch<64, 1>(a, stream);
+    if (d == 128 && g == 4) return merge_dispatch<128, 4>(a, stream, tm);
+    if (d == 128 && g == 2) return merge_dispatch<128, 2>(a, stream, tm);
+    if (d == 128 && g == 1) return merge_dispatch<128, 1>(a, stream, tm);
+    if (d == 64 && g == 4) return merge_dispatch<64, 4>(a, stream, tm);
+    if (d == 64 && g == 2) return merge_dispatch<64, 2>(a, stream, tm);
+    if (d == 64 && g == 1) return merge_dispatch<64, 1>(a, stream, tm);
     return hipErrorInvalidValue;
 }
 
