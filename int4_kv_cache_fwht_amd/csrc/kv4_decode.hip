@@ -220,7 +220,7 @@ struct DecodeWave {
     half4_t A4[NPAIR], A8[NPAIR];
     short4_t Abf[NPAIR_BF];
     float4_t acc[NHV][2]; // two accumulation chains per output half
-    float m[4], lsum[4], zsum[4], F[4], sumq[4];
+    float m[4], mt[4], lsum[4], zsum[4], F[4], sumq[4]; // mt = m + kTau, the rescale threshold
 
     __device__ DecodeWave(const DecodeArgs& args, int ln, uint8_t* lq, uint8_t* lp, int64_t wi, int64_t se)
         : a(args), lane(ln), lds_q(lq), lds_p(lp), w(wi), s_end(se),
@@ -235,6 +235,7 @@ struct DecodeWave {
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             m[i] = -INFINITY;
+            mt[i] = -INFINITY;
             lsum[i] = 0.f;
             zsum[i] = 0.f;
         }
@@ -364,12 +365,13 @@ struct DecodeWave {
     __device__ __forceinline__ void softmax_step(const float (&sc)[4], float lg, bool valid, float sVv, float zVv,
                                                  float (&pt)[4])
     {
+        // every caller passes sc = -inf on invalid lanes: their ep is -inf and their p is 0
         float ep[4];
         bool over = false;
 #pragma unroll
         for (int i = 0; i < G; i++) {
-            ep[i] = valid ? ((FMT == FMT_BF16) ? sc[i] : sc[i] + lg) : -INFINITY;
-            over |= ep[i] > m[i] + kTau;
+            ep[i] = (FMT == FMT_BF16) ? sc[i] : sc[i] + lg;
+            over |= ep[i] > mt[i];
         }
         if (__builtin_amdgcn_ballot_w64(over) != 0) {
             float mnew[4];
@@ -387,6 +389,7 @@ struct DecodeWave {
                     lsum[i] *= alpha;
                     zsum[i] *= alpha;
                     m[i] = in_vgpr(mnew[i]);
+                    mt[i] = in_vgpr(mnew[i] + kTau);
                 }
             }
         }
@@ -394,7 +397,7 @@ struct DecodeWave {
         for (int i = 0; i < 4; i++) {
             if (i < G) {
                 const float off = (m[i] == -INFINITY) ? 0.f : ((FMT == FMT_BF16) ? -m[i] : kPOffset - m[i]);
-                const float p = valid ? __builtin_amdgcn_exp2f(sc[i] + off) : 0.f;
+                const float p = __builtin_amdgcn_exp2f(sc[i] + off);
                 lsum[i] += p;
                 if (FMT != FMT_BF16) {
                     zsum[i] = fmaf(p, zVv, zsum[i]);
@@ -559,7 +562,8 @@ struct DecodeWave {
         float sc[4];
 #pragma unroll
         for (int i = 0; i < 4; i++) sc[i] = valid ? F[i] * fmaf(S[i], sK24, zK * sumq[i]) : -INFINITY;
-        const float lg = (sV > 0.f) ? __builtin_amdgcn_logf(sV) : -24.f;
+        // finite on invalid lanes (unspecified scale bits), so that their ep = sc + lg stays -inf
+        const float lg = (valid && sV > 0.f) ? __builtin_amdgcn_logf(sV) : -24.f;
         float pt[4];
         softmax_step(sc, lg, valid, valid ? sV : 0.f, valid ? zV : 0.f, pt);
 
@@ -636,7 +640,8 @@ struct DecodeWave {
         float sc[4];
 #pragma unroll
         for (int i = 0; i < 4; i++) sc[i] = valid ? F[i] * fmaf(S[i], sK24, zK * sumq[i]) : -INFINITY;
-        const float lg = (sV > 0.f) ? __builtin_amdgcn_logf(sV) : -24.f;
+        // finite on invalid lanes (unspecified scale bits), so that their ep = sc + lg stays -inf
+        const float lg = (valid && sV > 0.f) ? __builtin_amdgcn_logf(sV) : -24.f;
         float pt[4];
         softmax_step(sc, lg, valid, valid ? sV : 0.f, valid ? zV : 0.f, pt);
         exchange_h(pt, sl >> 2, sl & 3, lane_ok, false, Ahi, Alo);
