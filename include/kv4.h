@@ -243,9 +243,10 @@ kv4_status kv4_free_pages(kv4_cache_t h, int32_t* n);
 /* Tuning: number of waves the decode split kernel launches (0 = automatic). */
 kv4_status kv4_set_decode_waves(kv4_cache_t h, int32_t waves);
 
-/* Kernel timing (measurement of the hot path).  When enabled, every call records HIP events on
- * its own stream around each kernel it launches; kv4_profile_read waits for them and returns the
- * summed durations.  Enabling (or disabling) resets the totals.  Off by default. */
+/* Kernel timing (measurement of the hot path).  When enabled, each kernel a call launches on its
+ * stream stamps a pair of HIP events from its own dispatch (start, stop), so a duration is that
+ * kernel's execution alone; kv4_profile_read waits for them and returns the summed durations.
+ * Enabling (or disabling) resets the totals.  Off by default. */
 typedef struct kv4_profile {
     int64_t append_launches;
     double append_ms;  /* append kernels */
