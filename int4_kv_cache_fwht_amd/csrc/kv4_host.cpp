@@ -255,8 +255,21 @@ size_t decode_ws_bytes(const kv4_cache* h, int64_t n_units, int64_t waves)
            align_up((size_t)parts * G * D * sizeof(float));
 }
 
-// Multi-query split tasks: about two rounds of resident waves per call.
-int64_t mq_target_tasks(const kv4_cache* h) { return 2 * (int64_t)h->mq_resident_waves; }
+// Multi-query split tasks: three rounds of resident waves when no (sequence, kv head) has more
+// than 4 row tiles of kMqRows query rows, two rounds otherwise.  Smaller chunks balance the waves
+// of the few-tile calls; with many tiles per chunk they only add partials and re-reads (Qwen3-8B
+// layer on MI355X: 16 rows per sequence 336 against 372 us, 4 rows 127 against 132 us, 64 rows
+// 1196 us with two rounds against 1393 us with three).  n_q is read only where it is positive;
+// the call validates it.
+int64_t mq_target_tasks(const kv4_cache* h, int32_t n_seqs, const int32_t* n_q)
+{
+    const int G = h->st.cfg.hq / h->st.cfg.hkv;
+    int64_t tiles = 0;
+    if (n_q)
+        for (int32_t i = 0; i < n_seqs; i++)
+            if (n_q[i] > 0) tiles = std::max<int64_t>(tiles, ((int64_t)n_q[i] * G + kv4::kMqRows - 1) / kv4::kMqRows);
+    return (tiles <= 4 ? 3 : 2) * (int64_t)h->mq_resident_waves;
+}
 
 size_t mq_ws_bytes(const kv4_cache* h, const kv4::MqPlan& p)
 {
@@ -646,7 +659,7 @@ kv4_status kv4_multi_query_workspace_size(kv4_cache_t h, int32_t n_seqs, const i
     if (!h || !bytes) return fail(h, KV4_ERR_INVALID_ARGUMENT, "null argument");
     kv4::MqPlan plan;
     std::string msg;
-    kv4::Status s = h->st.plan_multi(n_seqs, seq_ids, n_q, mq_target_tasks(h), &plan, &msg);
+    kv4::Status s = h->st.plan_multi(n_seqs, seq_ids, n_q, mq_target_tasks(h, n_seqs, n_q), &plan, &msg);
     if (s != kv4::OK) return fail(h, (kv4_status)s, msg);
     *bytes = mq_ws_bytes(h, plan);
     return KV4_OK;
@@ -662,7 +675,7 @@ kv4_status kv4_multi_query_attention(kv4_cache_t h, int32_t n_seqs, const int32_
     if (!std::isfinite(scale)) return fail(h, KV4_ERR_INVALID_ARGUMENT, "scale must be finite");
     kv4::MqPlan plan;
     std::string msg;
-    kv4::Status s = h->st.plan_multi(n_seqs, seq_ids, n_q, mq_target_tasks(h), &plan, &msg);
+    kv4::Status s = h->st.plan_multi(n_seqs, seq_ids, n_q, mq_target_tasks(h, n_seqs, n_q), &plan, &msg);
     if (s != kv4::OK) return fail(h, (kv4_status)s, msg);
     if (plan.entries.empty()) return KV4_OK;
     if (!workspace || ws_bytes < mq_ws_bytes(h, plan))
