@@ -228,16 +228,11 @@ struct DeviceGuard {
     }
 };
 
-// Decode split waves: one full round of resident waves, or two rounds when every wave would
-// otherwise get many steps (the second round then evens out the tail).  A partial extra round is
-// never used: its waves would finish late.
-constexpr int64_t kStepsForTwoRounds = 32;
-
-int64_t auto_waves(const kv4_cache* h, int64_t total_steps)
-{
-    const int64_t cap = h->resident_waves;
-    return total_steps >= kStepsForTwoRounds * cap ? 2 * cap : cap;
-}
+// Decode split waves: one full round of resident waves.  With the issue-priority feedback between
+// the two waves of a SIMD, a second round no longer pays: on MI355X the 8 x 128K-token call takes
+// 205 + 6 us (split + merge) in one round against 210 + 11 us in two, the 256-sequence rollout
+// call 356 + 9 against 359 + 8 us, and the 64-sequence Qwen3-8B layer 71 against 76 us.
+int64_t auto_waves(const kv4_cache* h, int64_t /*total_steps*/) { return h->resident_waves; }
 
 int64_t max_waves(const kv4_cache* h)
 {
