@@ -71,7 +71,9 @@ __device__ __forceinline__ QuantParams quant_params(float mn, float mx, float Qf
     return p;
 }
 
-template <int D, int FMT>
+// ROT: 0 no rotation (block 1, and the BF16 format), 2 the full block (block == D: every stage,
+// with no test between them), 1 any other block (stages tested against the block at run time).
+template <int D, int FMT, int ROT>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FMT == FMT_INT4_PROT ? 4 : 1))) void append_kernel(AppendArgs a)
 {
     constexpr int N = D / 2; // values per lane
@@ -184,20 +186,25 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(FMT == FMT_I
             }
         }
         // stages h = 1, 2, ..., b/2 in that order: h < Q inside each quarter block, h = Q across
-        // the lane pair, h = D/2 between the lane's two quarter blocks
-        fwht_in_lane<N>(y, a.block < Q ? a.block : Q);
-        if (a.block > Q) fwht_across_pair<N>(y, half);
-        if (a.block > D / 2) {
+        // the lane pair, h = D/2 between the lane's two quarter blocks.  With the block a run-time
+        // value, every stage is a branch and the 64 values are copied into place at each join; the
+        // full block (the usual case) has the stages unconditional.
+        if constexpr (ROT != 0) {
+            const int b = (ROT == 2) ? D : a.block;
+            fwht_in_lane<N>(y, b < Q ? b : Q);
+            if (b > Q) fwht_across_pair<N>(y, half);
+            if (b > D / 2) {
 #pragma unroll
-            for (int i = 0; i < Q; i++) {
-                const float a0 = y[i], c0 = y[i + Q];
-                y[i] = a0 + c0;
-                y[i + Q] = a0 - c0;
+                for (int i = 0; i < Q; i++) {
+                    const float a0 = y[i], c0 = y[i + Q];
+                    y[i] = a0 + c0;
+                    y[i + Q] = a0 - c0;
+                }
             }
-        }
-        if (a.block > 1) {
+            if (b > 1) {
 #pragma unroll
-            for (int i = 0; i < N; i++) y[i] = y[i] * a.cb;
+                for (int i = 0; i < N; i++) y[i] = y[i] * a.cb;
+            }
         }
         // ---- row min / max ----
         float mn = y[0], mx = y[0];
@@ -613,8 +620,14 @@ hipError_t launch_append(int d, int format, int n_tasks, const AppendArgs& a, hi
 {
     if (n_tasks <= 0) return hipSuccess;
     dim3 grid((unsigned)n_tasks, (unsigned)a.hkv), block(64);
-#define KV4_APPEND_CASE(DD, FF) \
-    if (d == DD && format == FF) return launch_kernel(append_kernel<DD, FF>, grid, block, stream, tm, a);
+#define KV4_APPEND_CASE(DD, FF)                                                                     \
+    if (d == DD && format == FF) {                                                                  \
+        if (FF == FMT_BF16 || a.block <= 1)                                                         \
+            return launch_kernel(append_kernel<DD, FF, 0>, grid, block, stream, tm, a);             \
+        if (FF != FMT_BF16 && a.block == DD)                                                        \
+            return launch_kernel(append_kernel<DD, FF, FF == FMT_BF16 ? 0 : 2>, grid, block, stream, tm, a); \
+        return launch_kernel(append_kernel<DD, FF, FF == FMT_BF16 ? 0 : 1>, grid, block, stream, tm, a); \
+    }
     KV4_APPEND_CASE(64, 0)
     KV4_APPEND_CASE(64, 1)
     KV4_APPEND_CASE(64, 2)
