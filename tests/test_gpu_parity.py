@@ -48,7 +48,9 @@ def test_tiny_prefill_and_incremental():
     (kv4.FORMAT_INT4_PROT, 128, 4, 0),    # sinks only
     (kv4.FORMAT_INT4_PROT, 128, 0, 128),  # recent window only
     (kv4.FORMAT_INT4_PROT, 1, 4, 128),    # protection without rotation
+    (kv4.FORMAT_INT4_PROT, 64, 4, 16),    # half block: the lane-pair stage, not the last one
     (kv4.FORMAT_INT8, 128, 0, 0),
+    (kv4.FORMAT_INT8, 16, 0, 0),          # partial block of the INT8 format
     (kv4.FORMAT_BF16, 1, 0, 0),
 ])
 def test_ragged_batch(fmt, b, S, R):
