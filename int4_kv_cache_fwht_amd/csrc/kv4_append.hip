@@ -504,11 +504,9 @@ __global__ __launch_bounds__(64) void append_token_kernel(AppendArgs a)
     static_for<0, 5>([&](auto S) {
         constexpr int M = 1 << S;
         if (M * PL < a.block) {
+            const float sgn = (l32 & M) ? -1.f : 1.f;
 #pragma unroll
-            for (int i = 0; i < PL; i++) {
-                const float other = lane_xor<M>(y[i]);
-                y[i] = (l32 & M) ? other - y[i] : y[i] + other;
-            }
+            for (int i = 0; i < PL; i++) y[i] = butterfly_xor<M>(y[i], sgn);
         }
     });
     if (a.block > 1) {

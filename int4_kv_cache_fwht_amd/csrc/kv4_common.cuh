@@ -93,7 +93,7 @@ __device__ __forceinline__ uint32_t f16_round_up(float x)
 // Value of lane (lane ^ 1).
 __device__ __forceinline__ float dpp_xor1(float x)
 {
-    return as_float((uint32_t)__builtin_amdgcn_update_dpp(0, (int)as_uint(x), 0xB1, 0xF, 0xF, false));
+    return as_float((uint32_t)__builtin_amdgcn_mov_dpp((int)as_uint(x), 0xB1, 0xF, 0xF, false));
 }
 
 // Value of lane l ^ M of x within each row of 16 lanes (M = 1, 2, 4, 8), by DPP moves (no LDS
@@ -106,14 +106,14 @@ __device__ __forceinline__ float lane_xor_row(float x)
     const int v = (int)as_uint(x);
     int r;
     if constexpr (M == 1) {
-        r = __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false);
+        r = __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);
     } else if constexpr (M == 2) {
-        r = __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false);
+        r = __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);
     } else if constexpr (M == 4) {
-        const int t = __builtin_amdgcn_update_dpp(v, v, 0x141, 0xF, 0xF, false);
-        r = __builtin_amdgcn_update_dpp(t, t, 0x1B, 0xF, 0xF, false);
+        const int t = __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false);
+        r = __builtin_amdgcn_mov_dpp(t, 0x1B, 0xF, 0xF, false);
     } else {
-        r = __builtin_amdgcn_update_dpp(v, v, 0x128, 0xF, 0xF, false);
+        r = __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false);
     }
     return as_float((uint32_t)r);
 }
@@ -135,6 +135,15 @@ __device__ __forceinline__ float lane_xor(float x)
         return lane_xor16(x);
     else
         return __shfl_xor(x, M, 64);
+}
+
+// One butterfly of a Hadamard stage across lanes l and l ^ M: x + x' on the lane without bit M,
+// x' - x on the lane with it (x' the partner's value).  sgn is +1 or -1 to match; an fma with a
+// factor of +-1 rounds once, exactly like the add or the subtract it replaces.
+template <int M>
+__device__ __forceinline__ float butterfly_xor(float x, float sgn)
+{
+    return fmaf(sgn, x, lane_xor<M>(x));
 }
 
 // x[l] + x[l ^ 32] and max(x[l], x[l ^ 32]).  v_permlane32_swap of x with itself leaves the two

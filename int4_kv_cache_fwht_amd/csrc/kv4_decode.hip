@@ -261,13 +261,11 @@ struct DecodeWave {
         static_for<0, 6>([&](auto S) {
             constexpr int H = 1 << S;
             if (H < a.block) {
+                const float sgn = (lane & H) ? -1.f : 1.f;
 #pragma unroll
                 for (int i = 0; i < G; i++)
 #pragma unroll
-                    for (int j = 0; j < NHV; j++) {
-                        const float other = lane_xor<H>(qv[i][j]);
-                        qv[i][j] = (lane & H) ? other - qv[i][j] : qv[i][j] + other;
-                    }
+                    for (int j = 0; j < NHV; j++) qv[i][j] = butterfly_xor<H>(qv[i][j], sgn);
             }
         });
         if constexpr (NHV > 1) {
@@ -1027,11 +1025,9 @@ __global__ __launch_bounds__(64 * G) void merge_kernel(DecodeArgs a)
         static_for<0, 6>([&](auto S) {
             constexpr int H = 1 << S;
             if (H < a.block) {
+                const float sgn = (lane & H) ? -1.f : 1.f;
 #pragma unroll
-                for (int hv = 0; hv < NHV; hv++) {
-                    const float other = lane_xor<H>(r[hv]);
-                    r[hv] = (lane & H) ? other - r[hv] : r[hv] + other;
-                }
+                for (int hv = 0; hv < NHV; hv++) r[hv] = butterfly_xor<H>(r[hv], sgn);
             }
         });
         if constexpr (NHV > 1) {

@@ -238,12 +238,9 @@ struct MqWave {
         static_for<0, 2>([&](auto ST) {
             constexpr int MASK = 16 << ST;
             if ((DPL << ST) < a.block) {
-                const bool upper = (lane & MASK) != 0;
+                const float sgn = (lane & MASK) ? -1.f : 1.f;
 #pragma unroll
-                for (int i = 0; i < DPL; i++) {
-                    const float o = lane_xor<MASK>(x[i]);
-                    x[i] = upper ? o - x[i] : x[i] + o;
-                }
+                for (int i = 0; i < DPL; i++) x[i] = butterfly_xor<MASK>(x[i], sgn);
             }
         });
         float sum = 0.f, mx = 0.f;
@@ -669,12 +666,9 @@ __global__ __launch_bounds__(256) void mq_merge_kernel(MqArgs a)
         static_for<0, 6>([&](auto S) {
             constexpr int M = 1 << S;
             if (M * DPM < a.block) {
-                const bool upper = (lane & M) != 0;
+                const float sgn = (lane & M) ? -1.f : 1.f;
 #pragma unroll
-                for (int k = 0; k < DPM; k++) {
-                    const float other = lane_xor<M>(o[k]);
-                    o[k] = upper ? other - o[k] : o[k] + other;
-                }
+                for (int k = 0; k < DPM; k++) o[k] = butterfly_xor<M>(o[k], sgn);
             }
         });
 #pragma unroll
