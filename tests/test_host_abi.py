@@ -314,3 +314,28 @@ def test_no_bit_cast_of_vector_element_lvalue():
                     if pat.search(line):
                         bad.append("%s:%d: %s" % (name, i, line.strip()))
     assert not bad, bad
+
+
+def test_fma_with_unit_factor_is_the_add_or_subtract():
+    """The kernels' lane-exchange butterflies compute x' + x and x' - x as fmaf(+-1, x, x'): the
+    product by +-1 is exact, so the fma rounds once, like the add or subtract.  Checked here
+    bit for bit with the C library's fmaf over random, subnormal, signed-zero and large values."""
+    import ctypes
+    import ctypes.util
+    import numpy as np
+    libm = ctypes.CDLL(ctypes.util.find_library("m"))
+    libm.fmaf.argtypes = [ctypes.c_float, ctypes.c_float, ctypes.c_float]
+    libm.fmaf.restype = ctypes.c_float
+    rng = np.random.default_rng(7)
+    vals = list(rng.standard_normal(2000).astype(np.float32))
+    vals += list((rng.standard_normal(500) * 1e-40).astype(np.float32))  # subnormals
+    vals += list((rng.standard_normal(500) * 3e38).astype(np.float32))
+    vals += [np.float32(0.0), np.float32(-0.0), np.float32(1.0), np.float32(-1.0)]
+    vals = np.array(vals, dtype=np.float32)
+    a = vals
+    b = np.roll(vals, 17)
+    with np.errstate(over="ignore", invalid="ignore"):
+        for x, y in zip(a, b):
+            for sgn, ref in ((1.0, np.float32(y) + np.float32(x)), (-1.0, np.float32(y) - np.float32(x))):
+                got = np.float32(libm.fmaf(sgn, float(x), float(y)))
+                assert got.tobytes() == np.float32(ref).tobytes() or (np.isnan(got) and np.isnan(ref)), (x, y, sgn)
