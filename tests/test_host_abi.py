@@ -339,3 +339,14 @@ def test_fma_with_unit_factor_is_the_add_or_subtract():
             for sgn, ref in ((1.0, np.float32(y) + np.float32(x)), (-1.0, np.float32(y) - np.float32(x))):
                 got = np.float32(libm.fmaf(sgn, float(x), float(y)))
                 assert got.tobytes() == np.float32(ref).tobytes() or (np.isnan(got) and np.isnan(ref)), (x, y, sgn)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; --gpus N > 1 ends with a message, before any GPU work."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=300, cwd=root)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)
