@@ -182,3 +182,22 @@ def test_decode_bf16_output(fmt, b):
     assert np.array_equal(bits16, W.bf16_bits(torch.from_numpy(o32.astype(np.float32)).to(torch.bfloat16)))
     v16 = (bits16.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     assert np.all(np.abs(v16 - ref) <= TOL + np.abs(ref) * 2.0 ** -8)
+
+
+def test_decode_wave_counts():
+    """The split kernel at explicit wave counts: one wave (every unit in one slice), counts that
+    leave a workgroup partly empty (7, 13), and counts with slices shorter than a unit.  The
+    output must not depend on the partition beyond rounding order."""
+    _print_case("wave counts")
+    hq, hkv, d = 32, 8, 128
+    lens = [1, 17, 100, 132, 133, 300, 1000]
+    p = Pair(hq, hkv, d, num_pages=2048, max_seqs=16, max_pps=128, S=4, R=128, b=128)
+    ks, vs = zip(*[_kv(L, hkv, d, seed=3, idx=i) for i, L in enumerate(lens)])
+    p.append(list(range(len(lens))), lens, torch.cat(ks).contiguous(), torch.cat(vs).contiguous())
+    q = W.queries(len(lens), hq, d, seed=13, step=0, device="cuda")
+    for waves in (1, 7, 13, 64, 250, 0):
+        p.gpu.set_decode_waves(waves)
+        out, ref = p.decode(list(range(len(lens))), q)
+        err = np.abs(out - ref).max()
+        print("waves", waves, "max-abs", err, flush=True)
+        assert err <= TOL
