@@ -84,7 +84,7 @@ def kernel_source_hash():
     plain structs it includes, and the DecodeArgs struct of kv4_launch.h."""
     csrc = os.path.join(ROOT, "int4_kv_cache_fwht_amd", "csrc")
     h = hashlib.sha256()
-    for name in ("kv4_decode.hip", "kv4_common.cuh", "kv4_device_types.h"):
+    for name in ("kv4_decode.hip", "kv4_common.h", "kv4_device_types.h"):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     with open(os.path.join(csrc, "kv4_launch.h")) as f:

@@ -6,7 +6,7 @@
 //
 // Build with -ffp-contract=off: every binary32 step here must stay a single IEEE operation so that
 // codes and scales match the oracle bit for bit.
-#include "kv4_common.cuh"
+#include "kv4_common.h"
 
 namespace kv4 {
 
@@ -419,15 +419,19 @@ __global__ __launch_bounds__(64) void append_token_kernel(AppendArgs a)
 {
     constexpr int PL = D / 32; // dims per lane
     AppendTask tk;
-    // task e from the argument block, read in place from the kernarg segment (always present, so
-    // read before the test of n_arg: the loads do not wait for it)
+    // task e from the argument block, read in place from the kernarg segment before the test of
+    // n_arg (the loads do not wait for it).  With an uploaded task list the grid can exceed the
+    // kArgEntries entries of the block, so the index is clamped into it; those values are unused.
     const int e = blockIdx.x;
+    const int ea = e < kArgEntries ? e : 0;
     const __attribute__((address_space(4))) char* ka =
         (const __attribute__((address_space(4))) char*)__builtin_amdgcn_kernarg_segment_ptr();
-    const int32_t pg = ((const __attribute__((address_space(4))) int32_t*)(ka + offsetof(AppendArgs, arg_page)))[e];
-    const int32_t aseq = ((const __attribute__((address_space(4))) int32_t*)(ka + offsetof(AppendArgs, arg_seq)))[e];
-    const int32_t at0 = ((const __attribute__((address_space(4))) int32_t*)(ka + offsetof(AppendArgs, arg_t0)))[e];
+    const int32_t pg = ((const __attribute__((address_space(4))) int32_t*)(ka + offsetof(AppendArgs, arg_page)))[ea];
+    const int32_t aseq = ((const __attribute__((address_space(4))) int32_t*)(ka + offsetof(AppendArgs, arg_seq)))[ea];
+    const int32_t at0 = ((const __attribute__((address_space(4))) int32_t*)(ka + offsetof(AppendArgs, arg_t0)))[ea];
     if (a.n_arg > 0) {
+        // the host passes an argument plan only when every sequence of the call writes exactly
+        // one position, so the sequence's length after the call is t0 + 1
         tk.seq = aseq;
         tk.t0 = at0;
         tk.page = pg & 0x7FFFFFFF;

@@ -1,4 +1,4 @@
-// kv4_common.cuh -- device helpers shared by the libkv4 kernels (gfx950, wave64).
+// kv4_common.h -- device helpers shared by the libkv4 kernels (gfx950, wave64).
 #pragma once
 
 #include <hip/hip_ext.h>

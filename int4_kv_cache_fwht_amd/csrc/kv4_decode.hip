@@ -28,7 +28,7 @@
 // step's arithmetic and the wait counters never drain them.  Loads past the end repeat the last
 // step's addresses (cached lines) and are never used.  Page ids are read with scalar loads (their
 // own counter) two steps ahead.
-#include "kv4_common.cuh"
+#include "kv4_common.h"
 
 namespace kv4 {
 

@@ -436,11 +436,17 @@ kv4_status append_impl(kv4_cache_t h, int32_t n_seqs, const int32_t* seq_ids, co
     DeviceGuard g(h->device);
     if (g.err != hipSuccess) return hip_fail(h, g.err, "hipSetDevice");
     hipStream_t strm = (hipStream_t)stream;
-    // decode-time appends (one position per sequence) take the per-position kernel; up to
-    // kArgEntries of them travel in the kernel arguments instead of an uploaded task list
+    // calls whose tasks all write one position take the per-position kernel.  Up to kArgEntries
+    // of them travel in the kernel arguments instead of an uploaded task list, but only when no
+    // sequence has two tasks (n_new = 2 across a page boundary gives two): the argument plan does
+    // not carry the length after the call, and the kernel takes it as t0 + 1.
     bool single = h->st.cfg.format == kv4::FMT_INT4_PROT;
-    for (const auto& tk : tasks) single = single && tk.n == 1;
-    const bool argplan = single && tasks.size() <= (size_t)kv4::kArgEntries;
+    bool one_per_seq = true;
+    for (size_t i = 0; i < tasks.size(); i++) {
+        single = single && tasks[i].n == 1;
+        one_per_seq = one_per_seq && (i == 0 || tasks[i].seq != tasks[i - 1].seq);
+    }
+    const bool argplan = single && one_per_seq && tasks.size() <= (size_t)kv4::kArgEntries;
     hipError_t e = hipSuccess;
     if (!argplan) {
         const size_t bytes = tasks.size() * sizeof(kv4::AppendTask);

@@ -25,7 +25,7 @@
 // largest over a lane's positions); it is raised only when a step exceeds it by more than kMqTau
 // (then the accumulators are rescaled).  This bounds p * s_V * 2^27 below 2^14, inside the fp16
 // range, whatever the value scales.
-#include "kv4_common.cuh"
+#include "kv4_common.h"
 
 namespace kv4 {
 namespace {

@@ -37,6 +37,10 @@ class Pair:
         rc = self.ora.append_rope(seq_ids, n_new, bf16_bits(k), bf16_bits(v), cos, sin)
         assert rc == oracle.OK, rc
 
+    def seq_free(self, seq):
+        self.gpu.seq_free(seq)
+        assert self.ora.seq_free(seq) == oracle.OK
+
     def decode(self, seq_ids, q, scale=0.0):
         out = self.gpu.decode_attention(seq_ids, q, scale=scale)
         ref, _ = self.ora.decode(seq_ids, bf16_bits(q), scale=scale)

@@ -45,7 +45,7 @@ def _gpu_codes(cache, pool, i8, seq, t, h, kv):
     return out
 
 
-def _check_workload(name, sample_fn, positions_per_seq=12):
+def _check_workload(name, sample_fn, positions_per_seq=12, mq_rows=(4,)):
     w = W.WORKLOADS[name]
     dev = torch.device("cuda", 0)
     b = bench.Bench(w, "int4", 1, 2, dev, 0)
@@ -72,16 +72,17 @@ def _check_workload(name, sample_fn, positions_per_seq=12):
     print(name, "sampled sequences", sample, "lengths", [lens0[i] + 1 for i in sample], "max-abs", err,
           "oracle threads", used, flush=True)
     assert err <= TOL
-    # multi-query attention over the same cache: the last 4 positions of every sequence as causal
+    # multi-query attention over the same cache: the last nq positions of every sequence as causal
     # query rows, one call (its own work split); the oracle checks the sampled sequences
-    nq = 4
-    qm = W.queries(nq * len(lens0), hq, d, w.seed, step=99, device=dev)
-    outm = cache.multi_query_attention(list(range(len(lens0))), [nq] * len(lens0), qm).cpu().numpy()
-    rows = np.concatenate([np.arange(nq * i, nq * (i + 1)) for i in sample])
-    refm, _ = ora.attend_multi(list(range(len(sample))), [nq] * len(sample), bf16_bits(qm[torch.from_numpy(rows).to(dev)]))
-    errm = np.abs(outm[rows].astype(np.float64) - refm).max()
-    print(name, "multi-query (4 rows) sampled max-abs", errm, flush=True)
-    assert errm <= TOL
+    for nq in mq_rows:
+        qm = W.queries(nq * len(lens0), hq, d, w.seed, step=99 + nq, device=dev)
+        outm = cache.multi_query_attention(list(range(len(lens0))), [nq] * len(lens0), qm).cpu().numpy()
+        rows = np.concatenate([np.arange(nq * i, nq * (i + 1)) for i in sample])
+        refm, _ = ora.attend_multi(list(range(len(sample))), [nq] * len(sample),
+                                   bf16_bits(qm[torch.from_numpy(rows).to(dev)]))
+        errm = np.abs(outm[rows].astype(np.float64) - refm).max()
+        print(name, "multi-query (%d rows) sampled max-abs" % nq, errm, flush=True)
+        assert errm <= TOL
     # codes and scales of sampled positions, bit for bit
     sz = cache.sizes
     pool = cache.page_pool.cpu().numpy()[: sz.page_pool].reshape(cache.cfg.num_pages, hkv, sz.page_block_bytes)
@@ -110,7 +111,7 @@ def _check_workload(name, sample_fn, positions_per_seq=12):
 
 def test_qwen3_8b_layer_full_size():
     _print_case("qwen3_8b_layer full size")
-    _check_workload("qwen3_8b_layer", lambda L: [int(np.argmin(L)), int(np.argmax(L)), 17, 40])
+    _check_workload("qwen3_8b_layer", lambda L: [int(np.argmin(L)), int(np.argmax(L)), 17, 40], mq_rows=(4, 16))
 
 
 def test_rollout_layer_full_size():
@@ -120,7 +121,7 @@ def test_rollout_layer_full_size():
 
 def test_long_context_full_size():
     _print_case("long_context full size")
-    _check_workload("long_context", lambda L: [3])
+    _check_workload("long_context", lambda L: [0, 3, len(L) - 1])
 
 
 def test_append_workload_full():
@@ -222,12 +223,13 @@ def test_host_errors_leave_state_unchanged():
     assert c.free_pages() == 0
 
 
-def test_uploaded_plan_path():
-    """More sequences than the kernel arguments carry (300 > 256): the decode plan and the
-    single-position append tasks are uploaded instead.  Ragged lengths, two decode steps."""
-    _print_case("uploaded plan", n=300)
+@pytest.mark.parametrize("n", [300, 1024])
+def test_uploaded_plan_path(n):
+    """More sequences than the kernel arguments carry (300, 1024 > 256): the decode plan and the
+    single-position append tasks are uploaded instead (at 1024 the append grid runs far past the
+    argument block's entries).  Ragged lengths, two decode steps."""
+    _print_case("uploaded plan", n=n)
     hq, hkv, d = 8, 2, 64
-    n = 300
     rng = np.random.default_rng(9)
     lens = [int(x) for x in rng.integers(1, 200, n)]
     p = Pair(hq, hkv, d, num_pages=sum(math.ceil((L + 2) / 16) for L in lens) + n, max_seqs=n, max_pps=16,
@@ -244,4 +246,4 @@ def test_uploaded_plan_path():
         err = np.abs(out - ref).max()
         print("uploaded plan step", step, "max-abs", err, flush=True)
         assert err <= TOL
-    assert p.compare_cache([ids[0], ids[1], 17, 299]) > 0
+    assert p.compare_cache([ids[0], ids[1], 17, n - 1]) > 0
