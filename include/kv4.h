@@ -235,6 +235,24 @@ kv4_status kv4_decode_attention_bf16(kv4_cache_t h, int32_t n_seqs, const int32_
                                      float scale, void* out, void* workspace, size_t ws_bytes,
                                      void* stream /* hipStream_t */);
 
+/*
+ * kv4_decode_attention for callers that cannot allocate memory during the call (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the same computation,
+ * kernels and result bits as kv4_decode_attention with its automatic wave count, but the
+ * split-KV partials live in a device scratch array that the library holds, one per GPU, of
+ * 16 MiB, kept until the process ends (its address is looked up once per device by
+ * kv4_cache_create).  The call allocates nothing, host or device, and records no profiling events.
+ *   q (device) bf16 [n_seqs][Hq][D], out (device) fp32 [n_seqs][Hq][D], as kv4_decode_attention.
+ * Limits: n_seqs <= 256 (UNSUPPORTED beyond), and the call's partials (about (W + n_seqs * Hkv) *
+ * G * (D + 2) * 4 bytes, W = the split's wave count) must fit the 16 MiB (WORKSPACE_TOO_SMALL).
+ * Nothing in the scratch needs clearing between calls: every partial the merge reads is written by
+ * the same call.  All calls on one GPU share that GPU's scratch: calls that may overlap (on
+ * different streams, or from several handles or threads) race and must be ordered by the caller.
+ * Other errors as kv4_decode_attention.
+ */
+kv4_status kv4_decode_attention_noalloc(kv4_cache_t h, int32_t n_seqs, const int32_t* seq_ids, const void* q,
+                                        float scale, float* out, void* stream /* hipStream_t */);
+
 /* Host-state queries. */
 kv4_status kv4_seq_length(kv4_cache_t h, int32_t seq_id, int32_t* len);
 kv4_status kv4_block_table(kv4_cache_t h, int32_t seq_id, int32_t* pages /* host */, int32_t cap, int32_t* n);

@@ -116,6 +116,7 @@ def lib():
         L.kv4_decode_workspace_size.argtypes = [P, I32, P]
         L.kv4_decode_attention.argtypes = [P, I32, P, P, ctypes.c_float, P, P, SZ, P]
         L.kv4_decode_attention_bf16.argtypes = [P, I32, P, P, ctypes.c_float, P, P, SZ, P]
+        L.kv4_decode_attention_noalloc.argtypes = [P, I32, P, P, ctypes.c_float, P, P]
         L.kv4_multi_query_workspace_size.argtypes = [P, I32, P, P, P]
         L.kv4_multi_query_attention.argtypes = [P, I32, P, P, P, ctypes.c_float, P, P, SZ, P]
         L.kv4_seq_length.argtypes = [P, I32, P]
@@ -129,7 +130,8 @@ def lib():
         L.kv4_last_error.argtypes = [P]
         L.kv4_last_error.restype = ctypes.c_char_p
         for name in ("kv4_buffer_sizes_query", "kv4_cache_create", "kv4_cache_destroy", "kv4_append_workspace_size",
-                     "kv4_append", "kv4_append_rope", "kv4_seq_free", "kv4_decode_workspace_size", "kv4_decode_attention", "kv4_decode_attention_bf16",
+                     "kv4_append", "kv4_append_rope", "kv4_seq_free", "kv4_decode_workspace_size", "kv4_decode_attention",
+                     "kv4_decode_attention_bf16", "kv4_decode_attention_noalloc",
                      "kv4_multi_query_workspace_size", "kv4_multi_query_attention",
                      "kv4_seq_length", "kv4_block_table", "kv4_free_pages", "kv4_set_decode_waves",
                      "kv4_profile_enable", "kv4_profile_read"):
@@ -290,6 +292,23 @@ class Cache:
         st = _stream_ptr(stream)
         _check(lib().kv4_decode_attention(self._h, n, ids, q.data_ptr(), float(scale), out.data_ptr(),
                                           workspace.data_ptr(), workspace.numel(), st), self._h)
+        return out
+
+    def decode_attention_noalloc(self, seq_ids: Sequence[int], q: torch.Tensor, out: torch.Tensor,
+                                 scale: float = 0.0, stream=None) -> torch.Tensor:
+        """kv4_decode_attention_noalloc: q bf16 [n, Hq, D] -> out, a caller-given fp32 [n, Hq, D]
+        tensor (the call takes no workspace and allocates nothing)."""
+        ids = _i32_array(seq_ids)
+        n = len(ids)
+        shape = (n, self.cfg.num_q_heads, self.cfg.head_dim)
+        if q.dtype != torch.bfloat16 or not q.is_contiguous() or tuple(q.shape) != shape or q.device != self.device:
+            raise ValueError("q must be a contiguous bf16 [n, Hq, D] tensor on the cache device")
+        if out.dtype != torch.float32 or not out.is_contiguous() or tuple(out.shape) != shape \
+                or out.device != self.device:
+            raise ValueError("out must be a contiguous fp32 [n, Hq, D] tensor on the cache device")
+        st = _stream_ptr(stream)
+        _check(lib().kv4_decode_attention_noalloc(self._h, n, ids, q.data_ptr(), float(scale), out.data_ptr(), st),
+               self._h)
         return out
 
     def multi_query_workspace_size(self, seq_ids: Sequence[int], n_q: Sequence[int]) -> int:

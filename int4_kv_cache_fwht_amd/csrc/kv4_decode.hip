@@ -30,7 +30,38 @@
 // own counter) two steps ahead.
 #include "kv4_common.h"
 
+#include <mutex>
+
 namespace kv4 {
+
+// Device scratch of the allocation-free decode entry point: the split kernel's partials live here
+// instead of in a caller workspace.  One copy per GPU, held until the process ends.  Host code
+// never uses the array's name as an address: decode_scratch() looks up each device's copy once
+// (with that device current) and every later use goes through the pointer it returns.
+static __device__ __align__(256) uint8_t scratch[kDecodeScratchBytes];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices] = {};
+} // namespace
+
+hipError_t decode_scratch(void** ptr)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 constexpr int kLdsQBytes = 4 * 128 * 4; // rotated query, G x D fp32 (raw bf16 query first)
 constexpr int kLdsPBytes = 64 * 16;     // per-step probability exchange (fp32)

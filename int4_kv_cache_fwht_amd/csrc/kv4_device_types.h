@@ -11,6 +11,9 @@ constexpr int kInt8StepSlots = 32;  // decode INT8 step over protection slots: 2
 constexpr int kInt8StepPages = 2;   // decode step of the INT8 format: 2 pages = 32 positions
 constexpr int kWavesPerBlock = 8;   // decode split kernel: waves per workgroup (two per SIMD)
 constexpr int kArgEntries = 256;    // calls with up to this many sequences pass their plan as kernel arguments
+// Device scratch of the allocation-free decode entry point (one array per GPU): the largest decode
+// workspace it serves.
+constexpr unsigned long long kDecodeScratchBytes = 16ull << 20;
 // Decode split: every unit's step range opens with this many accounting steps that hold no work.
 // A wave whose slice starts a unit pays its query prologue, its epilogue and a refill of the load
 // pipeline; charging that as steps evens out the waves' finishing times (3 measured best on MI355X

@@ -169,6 +169,8 @@ struct kv4_cache {
     int mq_resident_waves = 2048; // multi-query split waves resident at once
     int decode_waves = 0; // 0: automatic
     float cb = 1.0f;
+    void* scratch = nullptr;                // this device's decode scratch (kDecodeScratchBytes)
+    std::vector<kv4::DecodeUnit> units_buf; // decode plan, reused (capacity for kArgEntries entries)
     Staging staging;
     Profiler prof;
     std::string err;
@@ -363,6 +365,14 @@ kv4_status kv4_cache_create(const kv4_config* cfg, const kv4_buffers* bufs, kv4_
         }
         h->mq_resident_waves = (bpc > 0 ? bpc : 1) * 4 * h->num_cus;
     }
+    // the allocation-free decode's scratch: looked up once per device, here where the device is
+    // current and the library's kernels are being loaded anyway
+    e = kv4::decode_scratch(&h->scratch);
+    if (e != hipSuccess) {
+        delete h;
+        return hip_fail(nullptr, e, "hipGetSymbolAddress(decode scratch)");
+    }
+    h->units_buf.reserve((size_t)kv4::kArgEntries * c.hkv);
     h->cb = (float)(1.0 / std::sqrt((double)c.block));
     e = h->staging.init(8);
     if (e != hipSuccess) {
@@ -545,14 +555,19 @@ kv4_status kv4_decode_workspace_size(kv4_cache_t h, int32_t n_seqs, size_t* byte
 
 namespace {
 
+// noalloc: the workspace is the device's decode scratch (workspace / ws_bytes ignored); the call
+// then allocates nothing, host or device: the plan goes in the kernel arguments (at most
+// kArgEntries sequences), the unit list reuses the handle's buffer, and no timing events are made.
 kv4_status decode_impl(kv4_cache_t h, int32_t n_seqs, const int32_t* seq_ids, const void* q, float scale, void* out_ptr,
-                       bool out16, void* workspace, size_t ws_bytes, void* stream)
+                       bool out16, void* workspace, size_t ws_bytes, void* stream, bool noalloc = false)
 {
     float* out = (float*)out_ptr;
     if (!h) return fail(nullptr, KV4_ERR_INVALID_ARGUMENT, "null handle");
     if (n_seqs < 0 || (n_seqs > 0 && (!seq_ids || !q || !out))) return fail(h, KV4_ERR_INVALID_ARGUMENT, "bad argument list");
     if (!std::isfinite(scale)) return fail(h, KV4_ERR_INVALID_ARGUMENT, "scale must be finite");
-    std::vector<kv4::DecodeUnit> units;
+    if (noalloc && n_seqs > kv4::kArgEntries)
+        return fail(h, KV4_ERR_UNSUPPORTED, "the allocation-free decode takes at most 256 sequences per call");
+    std::vector<kv4::DecodeUnit>& units = h->units_buf;
     int64_t total = 0;
     std::string msg;
     kv4::Status s = h->st.plan_decode(n_seqs, seq_ids, &units, &total, &msg);
@@ -563,6 +578,13 @@ kv4_status decode_impl(kv4_cache_t h, int32_t n_seqs, const int32_t* seq_ids, co
     if (W > total) W = total;
     if (W < 1) W = 1;
     const int64_t n_units = (int64_t)units.size();
+    if (noalloc) {
+        workspace = h->scratch;
+        ws_bytes = (size_t)kv4::kDecodeScratchBytes;
+        if (decode_ws_bytes(h, n_units, W) > ws_bytes)
+            return fail(h, KV4_ERR_WORKSPACE_TOO_SMALL,
+                        "the call needs more than the 16 MiB of device scratch of the allocation-free decode");
+    }
     if (!workspace || ws_bytes < decode_ws_bytes(h, n_units, W) || W > wmax)
         return fail(h, KV4_ERR_WORKSPACE_TOO_SMALL, "decode workspace too small");
 
@@ -572,6 +594,7 @@ kv4_status decode_impl(kv4_cache_t h, int32_t n_seqs, const int32_t* seq_ids, co
     const size_t ubytes = (size_t)n_units * sizeof(kv4::DecodeUnit);
     // up to kArgEntries sequences: the plan is the entry list in the kernel arguments (no upload)
     const bool argplan = n_seqs <= kv4::kArgEntries && total < ((int64_t)1 << 31);
+    if (noalloc && !argplan) return fail(h, KV4_ERR_UNSUPPORTED, "the allocation-free decode needs an argument plan");
     hipError_t e = hipSuccess;
     if (!argplan) {
         void* host = nullptr;
@@ -623,7 +646,8 @@ kv4_status decode_impl(kv4_cache_t h, int32_t n_seqs, const int32_t* seq_ids, co
     }
     std::vector<hipEvent_t> ev;
     kv4::KernelTimer t_split, t_merge;
-    if (h->prof.on) {
+    const bool timed = h->prof.on && !noalloc;
+    if (timed) {
         e = Profiler::make(4, &ev);
         if (e != hipSuccess) return hip_fail(h, e, "profiling event");
         t_split = kv4::KernelTimer{ev[0], ev[1]};
@@ -634,7 +658,7 @@ kv4_status decode_impl(kv4_cache_t h, int32_t n_seqs, const int32_t* seq_ids, co
     e = out16 ? kv4::launch_decode_merge_bf16(D, G, h->st.cfg.format, a, strm, t_merge)
               : kv4::launch_decode_merge(D, G, h->st.cfg.format, a, strm, t_merge);
     if (e != hipSuccess) return hip_fail(h, e, "decode merge launch");
-    if (h->prof.on) h->prof.decode_ev.push_back(ev);
+    if (timed) h->prof.decode_ev.push_back(ev);
     return KV4_OK;
 }
 
@@ -652,6 +676,12 @@ kv4_status kv4_decode_attention_bf16(kv4_cache_t h, int32_t n_seqs, const int32_
                                      float scale, void* out, void* workspace, size_t ws_bytes, void* stream)
 {
     return decode_impl(h, n_seqs, seq_ids, q, scale, out, true, workspace, ws_bytes, stream);
+}
+
+kv4_status kv4_decode_attention_noalloc(kv4_cache_t h, int32_t n_seqs, const int32_t* seq_ids, const void* q,
+                                        float scale, float* out, void* stream)
+{
+    return decode_impl(h, n_seqs, seq_ids, q, scale, out, false, nullptr, 0, stream, true);
 }
 
 kv4_status kv4_multi_query_workspace_size(kv4_cache_t h, int32_t n_seqs, const int32_t* seq_ids, const int32_t* n_q,

@@ -96,6 +96,9 @@ hipError_t launch_decode_merge(int d, int g, int format, const DecodeArgs& a, hi
 // The same merge writing bf16 output rows (a.out then points at bf16 [entries][hq][D]).
 hipError_t launch_decode_merge_bf16(int d, int g, int format, const DecodeArgs& a, hipStream_t stream,
                                     const KernelTimer& tm = KernelTimer{});
+// Address of the current device's decode scratch (kDecodeScratchBytes, 256-byte aligned), looked
+// up once per device; later calls return the kept pointer.
+hipError_t decode_scratch(void** ptr);
 // Workgroups of the split kernel (kWavesPerBlock waves each) that fit on one compute unit at once.
 hipError_t decode_split_residency(int d, int g, int format, int* blocks_per_cu);
 // Multi-query attention (INT4_PROT and INT8 formats): split kernel over the call's wave tasks,

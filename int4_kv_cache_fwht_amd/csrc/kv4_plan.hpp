@@ -159,6 +159,7 @@ struct State {
     std::deque<int32_t> free_list;
     std::vector<int32_t> len;       // [max_seqs]
     std::vector<int32_t> bt;        // [max_seqs * max_pps]
+    std::vector<uint8_t> mark;      // [max_seqs], all 0 between calls: duplicate-id test of plan_decode
 
     void init(const Config& c)
     {
@@ -167,6 +168,7 @@ struct State {
         for (int i = 0; i < c.num_pages; i++) free_list.push_back(i);
         len.assign((size_t)c.max_seqs, 0);
         bt.assign((size_t)c.max_seqs * c.max_pps, -1);
+        mark.assign((size_t)c.max_seqs, 0);
     }
 
     // Validates an append and, on success, builds its page tasks and commits the host state.
@@ -245,7 +247,8 @@ struct State {
     }
 
     // Decode plan: one unit per (call entry, kv head), with its step prefix.  Returns the total
-    // step count in *total.
+    // step count in *total.  Allocates nothing once `units` has the capacity for the call (the
+    // duplicate-id test uses the state's own marks and clears them again).
     Status plan_decode(int n_seqs, const int32_t* ids, std::vector<DecodeUnit>* units, int64_t* total,
                        std::string* msg)
     {
@@ -255,14 +258,31 @@ struct State {
         };
         if (n_seqs < 0) return bad(INVALID_ARGUMENT, "n_seqs < 0");
         if (n_seqs > 0 && !ids) return bad(INVALID_ARGUMENT, "null seq_ids");
-        std::vector<uint8_t> seen((size_t)cfg.max_seqs, 0);
-        for (int i = 0; i < n_seqs; i++) {
-            int s = ids[i];
-            if (s < 0 || s >= cfg.max_seqs) return bad(INVALID_ARGUMENT, "sequence id out of range");
-            if (seen[(size_t)s]) return bad(INVALID_ARGUMENT, "duplicate sequence id in one call");
-            seen[(size_t)s] = 1;
-            if (len[(size_t)s] < 1) return bad(SEQ_STATE, "decode of an empty sequence");
+        Status st = OK;
+        const char* why = nullptr;
+        int marked = 0;
+        for (; marked < n_seqs; marked++) {
+            int s = ids[marked];
+            if (s < 0 || s >= cfg.max_seqs) {
+                st = INVALID_ARGUMENT;
+                why = "sequence id out of range";
+                break;
+            }
+            if (mark[(size_t)s]) {
+                st = INVALID_ARGUMENT;
+                why = "duplicate sequence id in one call";
+                break;
+            }
+            mark[(size_t)s] = 1;
+            if (len[(size_t)s] < 1) {
+                st = SEQ_STATE;
+                why = "decode of an empty sequence";
+                marked++;
+                break;
+            }
         }
+        for (int i = 0; i < marked; i++) mark[(size_t)ids[i]] = 0;
+        if (st != OK) return bad(st, why);
         units->clear();
         int64_t acc = 0;
         for (int i = 0; i < n_seqs; i++) {
