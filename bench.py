@@ -1,21 +1,32 @@
 #!/usr/bin/env python3
 """Decode-step benchmark of the INT4 KV cache on one MI355X.
 
-One step = one pass of the hot path over one batch: append one new position to every sequence
-(fused rotation + quantization into the paged cache, INT8 protection of the newest positions)
-and then GQA decode attention over every sequence's full context.  The timed region holds
-exactly --steps steps, bracketed by device synchronization; inputs are resident in HBM.
+Default workload: the asynchronous-rollout regime -- 256 sequences with lognormal context lengths
+(median 4096, clipped to [256, 32768]) at Qwen3-8B attention shapes, where one step is 36
+identical-shape layers run in sequence.  Each layer has its own cache (36 distinct caches, about
+1.9 GB each, so no layer's reads are served by the 256 MB last-level cache).  Per layer the step
+appends one new position to every sequence (fused rotation + quantization into the paged cache,
+INT8 protection of the newest positions) and then runs GQA decode attention over every sequence's
+full context.  The timed region holds exactly --steps steps bracketed by device
+synchronization; inputs are resident in HBM.
 
-Prints ONE JSON line.  value = kv-tokens/s = (sum of context lengths attended per step) x steps /
-wall time.  roofline = the decode split-KV kernel's algorithmic bytes per launch / its average
-duration (HIP events recorded by the library on the call's stream), against the 8 TB/s HBM peak.
-cpu_baseline = the CPU oracle's decode on a bounded sample of the same workload.
+Prints ONE JSON line.
+- value = kv-tokens/s = (sum of context lengths attended per layer) x layers x steps / wall time.
+- roofline = the decode split-KV kernel's algorithmic bytes per launch / its mean duration over
+  >= 50 back-to-back decode-only launches (kernel-stamped HIP events on the call's stream), against
+  the 8 TB/s HBM peak and against the probed streaming-read ceiling of the device.
+- baselines = the same workload with INT8-only and bf16 KV caches (pools of 4 distinct caches).
+- workloads = the Qwen3-8B layer (64 sequences, 1K-8K) and long context (8 x 131072).
+- append = the append path alone, Hadamard block 128 against 1 (rotation overhead).
+- protection_cost = decode split time and bytes at (S, R) = (0, 0), (4, 0), (0, 128), (4, 128).
+- cpu_baseline = the CPU oracle's decode on a bounded sample of the same workload.
 """
 import argparse
 import hashlib
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -26,32 +37,48 @@ HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA
 METRIC = "INT4-KV decode attention kv-tokens/s and achieved HBM GB/s (% of MI355X peak)"
 FORMATS = {"int4": 0, "int8": 1, "bf16": 2}
+KERNELS = {"int4": "decode_split_kernel<128,4,INT4_PROT>", "int8": "decode_split_kernel<128,4,INT8>",
+           "bf16": "decode_split_kernel<128,4,BF16>"}
+DTYPE = "fp16 MFMA operands (u4/u8 codes exact, query hi+lo), fp32 softmax and accumulation"
+EXTRAS = ("probe", "baselines", "workloads", "append", "protection", "quality", "cpu")
+
+
+def log(msg):
+    print("bench: " + msg, file=sys.stderr, flush=True)
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=40)
-    ap.add_argument("--warmup", type=int, default=4)
-    ap.add_argument("--workload", default="qwen3_8b_layer",
-                    choices=["qwen3_8b_layer", "rollout", "long_context", "tiny", "append", "multi_query"],
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="rollout",
+                    choices=["rollout", "qwen3_8b_layer", "long_context", "tiny", "append", "multi_query"],
                     help="decode workloads; 'append': the append path alone at Hadamard block 128 vs 1; "
                          "'multi_query': causal multi-query attention on the Qwen3-8B-shaped layer")
+    ap.add_argument("--layers", type=int, default=0, help="layers per step (0: the workload's, 36 for rollout)")
+    ap.add_argument("--caches", type=int, default=0,
+                    help="distinct layer caches (0: one per layer, at least 4, so no cache fits the 256 MB MALL)")
+    ap.add_argument("--decode-launches", type=int, default=72, help="back-to-back decode-only launches timed")
+    ap.add_argument("--extras", default=",".join(EXTRAS),
+                    help="comma list of %s, or 'none'" % ",".join(EXTRAS))
+    ap.add_argument("--baselines", default="int8,bf16", help="comma list of baseline formats")
+    ap.add_argument("--baseline-caches", type=int, default=4)
     ap.add_argument("--mq-rows", type=int, default=4, help="query rows per sequence of the multi_query workload")
-    ap.add_argument("--caches", type=int, default=4, help="distinct layer caches cycled (defeats the 256 MB MALL)")
-    ap.add_argument("--baselines", default="int8,bf16", help="comma list of baseline formats ('' for none)")
-    ap.add_argument("--baseline-steps", type=int, default=12)
     ap.add_argument("--cpu-baseline-seconds", type=float, default=12.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-quality", action="store_true", help="skip the decode-error diagnostic")
     ap.add_argument("--decode-waves", type=int, default=0)
     ap.add_argument("--hadamard-block", type=int, default=0,
                     help="override the workload's Hadamard block (1 = plain INT4: no q / output rotation)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU run: write the measured decode traffic from two rocprofv3 --pmc output folders")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run a plain 1 GiB device copy (reference kernel for PMC byte counters)")
-    return ap.parse_args()
+                    help="also run one 1 GiB probe copy (the reference kernel for PMC byte counters)")
+    a = ap.parse_args()
+    a.extras = set() if a.extras in ("", "none") else set(a.extras.split(","))
+    bad = a.extras - set(EXTRAS)
+    if bad:
+        ap.error("unknown extras: %s" % ",".join(sorted(bad)))
+    return a
 
 
 def per_token_bytes(fmt, hkv, d):
@@ -63,20 +90,28 @@ def per_token_bytes(fmt, hkv, d):
     return hkv * 2 * d * 2
 
 
-def decode_bytes(fmt, lens, w):
+def decode_bytes(fmt, lens, w, sinks=None, recent=None):
     """Algorithmic HBM bytes of one decode launch: cached positions read once (INT4 pages for
     unprotected positions, INT8 for the protected ones), block-table entries, q in, out out."""
     hkv, d, hq = w.num_kv_heads, w.head_dim, w.num_q_heads
+    S = w.num_sinks if sinks is None else sinks
+    R = w.num_recent if recent is None else recent
     b4, b8 = per_token_bytes("int4", hkv, d), per_token_bytes("int8", hkv, d)
     total = 0
     for L in lens:
         if fmt == "int4":
-            p = min(L, w.num_sinks + w.num_recent)
+            p = min(L, S + R)
             total += (L - p) * b4 + p * b8
         else:
             total += L * per_token_bytes(fmt, hkv, d)
         total += math.ceil(L / 16) * 4 + hq * d * 2 + hq * d * 4
     return total
+
+
+def stats_us(ms_list):
+    us = [x * 1e3 for x in ms_list]
+    return {"mean": statistics.fmean(us), "median": statistics.median(us), "min": min(us), "max": max(us),
+            "launches": len(us)}
 
 
 def kernel_source_hash():
@@ -110,15 +145,20 @@ def measured_traffic(workload, fmt):
 
 
 class Bench:
-    def __init__(self, w, fmt, n_caches, total_steps, device, decode_waves):
+    """n_caches distinct layer caches of one workload; a step runs `layers` layers, layer j of step s
+    on cache (s * layers + j) % n_caches: append one position to every sequence, then decode."""
+
+    def __init__(self, w, fmt, n_caches, layers, total_steps, device, decode_waves, sinks=None, recent=None):
         import torch
         import int4_kv_cache_fwht_amd as kv4
         import kv4_inputs as W
         self.torch, self.kv4, self.W = torch, kv4, W
-        self.w, self.fmt, self.device = w, fmt, device
+        self.w, self.fmt, self.device, self.layers = w, fmt, device, layers
+        self.S = w.num_sinks if sinks is None else sinks
+        self.R = w.num_recent if recent is None else recent
         self.lens0 = w.lengths()
         B = w.batch
-        growth = math.ceil(total_steps / n_caches) + 1
+        growth = math.ceil(total_steps * layers / n_caches) + 1
         max_len = max(self.lens0) + growth
         pages = sum(math.ceil((L + growth) / 16) for L in self.lens0) + B
         self.channels = W.outlier_channels(w.num_kv_heads, w.head_dim, w.outlier_channels, w.seed)
@@ -126,7 +166,7 @@ class Bench:
         for c in range(n_caches):
             cfg = kv4.Config(num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
                              num_pages=pages, max_seqs=B, max_pages_per_seq=math.ceil(max_len / 16) + 1,
-                             num_sinks=w.num_sinks, num_recent=w.num_recent,
+                             num_sinks=self.S if fmt == "int4" else 0, num_recent=self.R if fmt == "int4" else 0,
                              hadamard_block=w.hadamard_block if fmt != "bf16" else 1, format=FORMATS[fmt])
             cache = kv4.Cache(cfg, device)
             if decode_waves:
@@ -135,14 +175,15 @@ class Bench:
             self.caches.append(cache)
             self.lens.append(list(self.lens0))
         self.ids = list(range(B))
-        # per-step inputs, resident before timing
+        # per-(step, layer) inputs, resident before timing
         self.kn, self.vn, self.q = [], [], []
         for s in range(total_steps):
-            k, v = W.seq_kv(w.num_kv_heads, w.head_dim, B, self.channels, w.outlier_scale, w.seed, 1000 + s, 0,
-                            device)
-            self.kn.append(k)
-            self.vn.append(v)
-            self.q.append(W.queries(B, w.num_q_heads, w.head_dim, w.seed, step=s, device=device))
+            for j in range(layers):
+                k, v = W.seq_kv(w.num_kv_heads, w.head_dim, B, self.channels, w.outlier_scale, w.seed,
+                                1000 + s * layers + j, 0, device)
+                self.kn.append(k)
+                self.vn.append(v)
+                self.q.append(W.queries(B, w.num_q_heads, w.head_dim, w.seed, layer=j, step=s, device=device))
         self.out = torch.empty((B, w.num_q_heads, w.head_dim), dtype=torch.float32, device=device)
         self.step_idx = 0
         torch.cuda.synchronize()
@@ -166,15 +207,20 @@ class Bench:
         torch.cuda.synchronize()
 
     def step(self):
-        """One step on the next cache; returns the kv-tokens attended."""
+        """One step (all its layers); returns the kv-tokens attended and the per-layer lengths."""
         s = self.step_idx
-        c = s % len(self.caches)
-        cache = self.caches[c]
-        cache.append(self.ids, [1] * len(self.ids), self.kn[s], self.vn[s])
-        cache.decode_attention(self.ids, self.q[s], out=self.out)
-        self.lens[c] = [L + 1 for L in self.lens[c]]
+        toks, lens = 0, []
+        for j in range(self.layers):
+            c = (s * self.layers + j) % len(self.caches)
+            cache = self.caches[c]
+            i = s * self.layers + j
+            cache.append(self.ids, [1] * len(self.ids), self.kn[i], self.vn[i])
+            cache.decode_attention(self.ids, self.q[i], out=self.out)
+            self.lens[c] = [L + 1 for L in self.lens[c]]
+            toks += sum(self.lens[c])
+            lens.append(self.lens[c])
         self.step_idx += 1
-        return sum(self.lens[c]), self.lens[c]
+        return toks, lens
 
     def timed(self, steps):
         torch = self.torch
@@ -186,30 +232,90 @@ class Bench:
         torch.cuda.synchronize()
         return time.perf_counter() - t0, toks
 
-    def profiled(self, steps):
-        """Steps with the library's kernel events on; returns (split avg s, merge avg s, append avg s,
-        algorithmic bytes per split launch averaged)."""
+    def _profiling(self, on):
         for c in self.caches:
-            c.profile_enable(True)
-        nbytes = 0
+            c.profile_enable(on)
+
+    def _durations(self, kind):
+        out = []
+        for c in self.caches:
+            out += c.profile_durations(kind)
+        return out
+
+    def profiled_steps(self, steps):
+        """Steps with the library's kernel events on: per-launch append, split and merge durations (ms)."""
+        self._profiling(True)
         for _ in range(steps):
-            _, lens = self.step()
-            nbytes += decode_bytes(self.fmt, lens, self.w)
-        tot = {"split_ms": 0.0, "merge_ms": 0.0, "append_ms": 0.0, "decode_launches": 0, "append_launches": 0}
+            self.step()
+        d = {k: self._durations(k) for k in ("append", "split", "merge")}
+        self._profiling(False)
+        return d
+
+    def decode_only(self, launches):
+        """`launches` back-to-back decode calls (no appends), cycling the caches: per-launch split and
+        merge durations (ms) and the mean algorithmic bytes per launch."""
+        self._profiling(True)
+        nbytes = 0
+        q = self.q[0]
+        for i in range(launches):
+            c = i % len(self.caches)
+            self.caches[c].decode_attention(self.ids, q, out=self.out)
+            nbytes += decode_bytes(self.fmt, self.lens[c], self.w, self.S, self.R)
+        d = {k: self._durations(k) for k in ("split", "merge")}
+        self._profiling(False)
+        return d["split"], d["merge"], nbytes / launches
+
+    def close(self):
         for c in self.caches:
-            p = c.profile_read()
-            for k in tot:
-                tot[k] += p[k]
-            c.profile_enable(False)
-        n = max(tot["decode_launches"], 1)
-        return (tot["split_ms"] / n * 1e-3, tot["merge_ms"] / n * 1e-3,
-                tot["append_ms"] / max(tot["append_launches"], 1) * 1e-3, nbytes / n)
+            c.close()
+        self.caches = []
+
+
+def run_decode_workload(w, fmt, n_caches, layers, steps, warmup, launches, device, decode_waves=0, sinks=None,
+                        recent=None):
+    """Timed steps, then back-to-back decode-only launches.  Returns a record."""
+    import torch
+    b = Bench(w, fmt, n_caches, layers, warmup + steps + 2, device, decode_waves, sinks, recent)
+    for _ in range(warmup):
+        b.step()
+    el, toks = b.timed(steps)
+    prof = b.profiled_steps(2)
+    split, merge, bytes_launch = b.decode_only(launches)
+    b.close()
+    del b
+    torch.cuda.empty_cache()
+    st = stats_us(split)
+    ach = bytes_launch / (st["mean"] * 1e-6) / 1e9
+    return {"kv_tokens_per_s": toks / el, "ms_per_step": el / steps * 1e3, "wall_s": el, "kv_tokens": toks,
+            "split_us": st, "merge_us": stats_us(merge), "algorithmic_bytes_per_launch": bytes_launch,
+            "achieved_GBps": ach, "frac": ach / HBM_PEAK_GBPS,
+            "achieved_GBps_median": bytes_launch / (st["median"] * 1e-6) / 1e9,
+            "step_kernels_us": {"append": stats_us(prof["append"])["mean"], "split": stats_us(prof["split"])["mean"],
+                                "merge": stats_us(prof["merge"])["mean"]}}
+
+
+def hbm_probe(device, reps=20):
+    """Ceiling: hand-written streaming read of a 4 GiB buffer and copy of 2 GiB (median of reps)."""
+    import torch
+    import int4_kv_cache_fwht_amd as kv4
+    n = 4 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=device)
+    src.fill_(1)
+    dst = torch.empty(n // 2, dtype=torch.uint8, device=device)
+    kv4.hbm_probe(0, src, dst, n, 2)  # warm-up
+    rd = kv4.hbm_probe(0, src, dst, n, reps)
+    cp = kv4.hbm_probe(1, src, dst, n // 2, reps)
+    del src, dst
+    torch.cuda.empty_cache()
+    rmed, cmed = statistics.median(rd), statistics.median(cp)
+    return {"read_GBps": n / (rmed * 1e-3) / 1e9, "read_GBps_best": n / (min(rd) * 1e-3) / 1e9,
+            "copy_GBps": 2 * (n // 2) / (cmed * 1e-3) / 1e9, "buffer_bytes": n, "reps": reps,
+            "kernel": "kv4::probe_read_kernel / probe_copy_kernel (16-byte nontemporal loads, 8 in flight per lane)"}
 
 
 def cpu_baseline(w, seconds, device):
     """The oracle's decode (fp64, threaded) on a bounded sample of the workload: the first sequences
     of layer 0, decoded repeatedly for about `seconds` of CPU time."""
-    import torch
     import kv4_inputs as W
     import oracle
     lens = w.lengths()
@@ -234,8 +340,9 @@ def cpu_baseline(w, seconds, device):
             break
     toks = reps * sum(lens[:n_s])
     return {"value": toks / el, "unit": "kv-tokens/s", "cores": used, "kind": "oracle",
-            "sample": "%d sequences (%d positions) of %s, oracle decode in fp64 repeated %d times (%.1f s)" % (
-                n_s, sum(lens[:n_s]), w.name, reps, el)}
+            "sample": "%d sequences (%d positions) of %s layer 0, oracle decode in fp64 repeated %d times (%.1f s); "
+                      "the layers are identical in shape, so the rate applies per layer" % (
+                          n_s, sum(lens[:n_s]), w.name, reps, el)}
 
 
 QUALITY_VARIANTS = [
@@ -289,32 +396,15 @@ def quality(w, device, n_seqs=4):
         res[name] = {"max_abs": float(np.abs(err).max()),
                      "rel_rms": float(np.sqrt((err ** 2).mean() / (ref ** 2).mean()))}
         del cache
-    return {"reference": "exact fp64 attention on the unquantized bf16 K/V, %d sequences (%d positions)" % (
-        len(lens), sum(lens)), "errors": res}
-
-
-def copy_probe(device):
-    """Plain device copy of 1 GiB (the reference kernel for PMC byte counters) -> GB/s moved."""
-    import torch
-    n = 1 << 30
-    a = torch.empty(n, dtype=torch.uint8, device=device)
-    b = torch.empty_like(a)
-    b.copy_(a)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    reps = 5
-    for _ in range(reps):
-        b.copy_(a)
-    torch.cuda.synchronize()
-    el = time.perf_counter() - t0
-    del a, b
-    return 2 * n * reps / el / 1e9
+    return {"reference": "exact fp64 attention on the unquantized bf16 K/V of %s, %d sequences (%d positions)" % (
+        w.name, len(lens), sum(lens)), "errors": res}
 
 
 def append_workload(device, repeats=7):
     """The append path alone: 256 empty sequences x 512 single-position steps, and a bulk prefill of
     32768 positions into one sequence, timed with the rotation (b = 128), without it (b = 1, plain
-    INT4), and with the fused RoPE of pre-RoPE keys (b = 128).  Returns the JSON record."""
+    INT4), and with the fused RoPE of pre-RoPE keys (b = 128); variants interleaved per repeat, best
+    (minimum) of the per-repeat means."""
     import torch
     import int4_kv_cache_fwht_amd as kv4
     import kv4_inputs as W
@@ -325,20 +415,21 @@ def append_workload(device, repeats=7):
     rows = [W.seq_kv(hkv, d, B, ch, w.outlier_scale, w.seed, 2000 + s, 0, device) for s in range(steps)]
     kb, vb = W.seq_kv(hkv, d, bulk, ch, w.outlier_scale, w.seed, 3000, 0, device)
     cos, sin = (torch.from_numpy(t).to(device) for t in W.rope_tables(bulk + 1, d))
-    res = {}
-    for name, block, rope in (("b128", 128, False), ("b1", 1, False), ("b128_rope", 128, True)):
-        cfg = kv4.Config(num_q_heads=hq, num_kv_heads=hkv, head_dim=d, num_pages=B * (steps // 16) + bulk // 16 + 16,
-                         max_seqs=B + 1, max_pages_per_seq=bulk // 16 + 1, num_sinks=w.num_sinks,
-                         num_recent=w.num_recent, hadamard_block=block, format=0)
+    variants = (("b128", 128, False), ("b1", 1, False), ("b128_rope", 128, True))
+    res = {name: [[], []] for name, _, _ in variants}
+    for _ in range(repeats):
+        for name, block, rope in variants:
+            cfg = kv4.Config(num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+                             num_pages=B * (steps // 16) + bulk // 16 + 16, max_seqs=B + 1,
+                             max_pages_per_seq=bulk // 16 + 1, num_sinks=w.num_sinks, num_recent=w.num_recent,
+                             hadamard_block=block, format=0)
 
-        def app(cache, ids, n, k, v):
-            if rope:
-                cache.append_rope(ids, n, k, v, cos, sin)
-            else:
-                cache.append(ids, n, k, v)
+            def app(cache, ids, n, k, v):
+                if rope:
+                    cache.append_rope(ids, n, k, v, cos, sin)
+                else:
+                    cache.append(ids, n, k, v)
 
-        best_steps = best_bulk = float("inf")
-        for _ in range(repeats):
             cache = kv4.Cache(cfg, device)
             ids = list(range(B))
             app(cache, ids, [1] * B, rows[0][0], rows[0][1])  # warm-up of the launch path
@@ -348,28 +439,48 @@ def append_workload(device, repeats=7):
             cache.profile_enable(True)
             for s in range(steps):
                 app(cache, ids, [1] * B, rows[s][0], rows[s][1])
-            p = cache.profile_read()
-            best_steps = min(best_steps, p["append_ms"] / p["append_launches"] * 1e3)
+            res[name][0].append(statistics.fmean(cache.profile_durations("append")) * 1e3)
             cache.profile_enable(True)
             app(cache, [B], [bulk], kb, vb)
-            p = cache.profile_read()
-            best_bulk = min(best_bulk, p["append_ms"] * 1e3)
+            res[name][1].append(cache.profile_durations("append")[0] * 1e3)
             cache.profile_enable(False)
-            del cache
-        res[name] = (best_steps, best_bulk)
-    (s128, b128), (s1, b1), (sr, br) = res["b128"], res["b1"], res["b128_rope"]
+            cache.close()
+    best = {k: (min(v[0]), min(v[1])) for k, v in res.items()}
+    (s128, b128), (s1, b1), (sr, br) = best["b128"], best["b1"], best["b128_rope"]
     bulk_bytes = bulk * hkv * d * 2 * 2 + bulk * hkv * 2 * (d // 2 + 4)   # bf16 in, INT4 + scales out
-    return {"metric": "INT4 KV append (rotation + quantization + pack) tokens/s", "value": B / (s128 * 1e-6),
-            "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": 1, "ms_per_step": s128 * 1e-3,
-            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-            "config": {"workload": "append", "sequences": B, "steps": steps, "bulk_prefill": bulk, "kv_heads": hkv,
-                       "head_dim": d, "sinks": w.num_sinks, "recent": w.num_recent},
+    step_bytes = B * hkv * d * 2 * 2 + B * hkv * 2 * (d // 2 + 4) + B * hkv * 2 * (d + 4)  # + INT8 copy
+    return {"config": {"sequences": B, "steps": steps, "bulk_prefill": bulk, "kv_heads": hkv, "head_dim": d,
+                       "sinks": w.num_sinks, "recent": w.num_recent},
+            "tokens_per_s_b128": B / (s128 * 1e-6),
             "append_step_us": {"b128": s128, "b1": s1, "rotation_overhead": s128 / s1 - 1.0,
-                               "b128_fused_rope": sr, "fused_rope_overhead": sr / s128 - 1.0},
+                               "b128_fused_rope": sr, "fused_rope_overhead": sr / s128 - 1.0,
+                               "GBps_b128": step_bytes / (s128 * 1e-6) / 1e9},
             "bulk_prefill_us": {"b128": b128, "b1": b1, "rotation_overhead": b128 / b1 - 1.0,
-                                "GBps_b128": bulk_bytes / (b128 * 1e-6) / 1e9, "b128_fused_rope": br,
-                                "fused_rope_overhead": br / b128 - 1.0},
-            "note": "best of %d repeats; kernel time from HIP events on the call's stream" % repeats}
+                                "GBps_b128": bulk_bytes / (b128 * 1e-6) / 1e9,
+                                "frac_b128": bulk_bytes / (b128 * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+                                "b128_fused_rope": br, "fused_rope_overhead": br / b128 - 1.0},
+            "algorithmic_bytes": {"bulk_prefill": bulk_bytes, "step": step_bytes},
+            "note": "kernel time from kernel-stamped HIP events; per variant the minimum over %d interleaved "
+                    "repeats of (mean over the 512 step launches) and of the prefill launch" % repeats}
+
+
+def protection_cost(device, launches=48, n_caches=4):
+    """Decode split time and algorithmic bytes on the Qwen3-8B layer with no protection, sinks only,
+    recent window only and both (INT4 + INT8 protection), b = 128."""
+    import kv4_inputs as W
+    w = W.WORKLOADS["qwen3_8b_layer"]
+    out = {}
+    for S, R in ((0, 0), (4, 0), (0, 128), (4, 128)):
+        r = run_decode_workload(w, "int4", n_caches, 1, 4, 1, launches, device, sinks=S, recent=R)
+        out["S%d_R%d" % (S, R)] = {"split_us": r["split_us"]["mean"], "split_us_median": r["split_us"]["median"],
+                                   "algorithmic_bytes_per_launch": r["algorithmic_bytes_per_launch"],
+                                   "achieved_GBps": r["achieved_GBps"], "frac": r["frac"]}
+    base = out["S0_R0"]
+    for v in out.values():
+        v["time_vs_unprotected"] = v["split_us"] / base["split_us"] - 1.0
+        v["bytes_vs_unprotected"] = v["algorithmic_bytes_per_launch"] / base["algorithmic_bytes_per_launch"] - 1.0
+    return {"workload": "qwen3_8b_layer", "launches": launches, "variants": out}
+
 
 def mq_workload(device, n_q, steps, warmup, n_caches=4):
     """Multi-query attention on the Qwen3-8B-shaped layer (64 sequences, lengths uniform in
@@ -432,13 +543,13 @@ def mq_workload(device, n_q, steps, warmup, n_caches=4):
         ls = one()
         nbytes += decode_bytes("int4", ls, w) + len(ls) * (n_q - 1) * hq * d * 6
         flops += sum(n_q * L - n_q * (n_q - 1) // 2 for L in ls) * hq * 4 * d
-    tot = {"mq_split_ms": 0.0, "mq_merge_ms": 0.0, "append_ms": 0.0, "mq_launches": 0, "append_launches": 0}
+    split, merge, app = [], [], []
     for c in caches:
-        p = c.profile_read()
-        for k in tot:
-            tot[k] += p[k]
+        split += c.profile_durations("mq_split")
+        merge += c.profile_durations("mq_merge")
+        app += c.profile_durations("append")
         c.profile_enable(False)
-    split_s = tot["mq_split_ms"] / tot["mq_launches"] * 1e-3
+    split_s = statistics.fmean(split) * 1e-3
     bytes_launch, flops_launch = nbytes / prof_steps, flops / prof_steps
     gbps = bytes_launch / split_s / 1e9
     tflops = flops_launch / split_s / 1e12
@@ -450,25 +561,25 @@ def mq_workload(device, n_q, steps, warmup, n_caches=4):
         roof = {"bound": "mfma", "achieved": tflops, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": tflops / MFMA_F16_PEAK_TFLOPS}
     roof.update({"traffic": None, "kernel": "mq_split_kernel<128,4,INT4_PROT>", "avg_launch_us": split_s * 1e6,
+                 "median_launch_us": statistics.median(split) * 1e3,
                  "algorithmic_bytes_per_launch": bytes_launch, "algorithmic_flops_per_launch": flops_launch,
                  "achieved_GBps": gbps, "achieved_TFLOPs": tflops, "flops_per_byte": intensity})
     return {"metric": "INT4-KV multi-query attention: attended (query row, position) pairs per s", "value":
             attended / el, "unit": "row-positions/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
             "ms_per_step": el / steps * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-            "dtype": "f32", "data": "synthetic",
+            "dtype": DTYPE, "data": "synthetic",
             "config": {"workload": "multi_query", "batch": B, "query_rows_per_seq": n_q, "kv_heads": hkv,
                        "q_heads": hq, "head_dim": d, "context": "uniform[1024, 8192] + growth", "sinks": w.num_sinks,
                        "recent": w.num_recent, "hadamard_block": w.hadamard_block, "distinct_caches": n_caches},
             "roofline": roof,
-            "step_breakdown_us": {"append": tot["append_ms"] / max(tot["append_launches"], 1) * 1e3,
-                                  "mq_split": split_s * 1e6,
-                                  "mq_merge": tot["mq_merge_ms"] / tot["mq_launches"] * 1e3}}
+            "step_breakdown_us": {"append": statistics.fmean(app) * 1e3, "mq_split": split_s * 1e6,
+                                  "mq_merge": statistics.fmean(merge) * 1e3}}
 
 
 def write_traffic(fetch_dir, write_dir, workload, fmt="int4"):
     """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE; both with
     --copy-calibration) into the measured HBM bytes per decode-split launch, each counter scaled by
-    what it reads for the plain 1 GiB copy; stores them, keyed by the decode sources' hash, in
+    what it reads for the 1 GiB probe copy; stores them, keyed by the decode sources' hash, in
     profiles/decode_split_traffic.json."""
     import csv
     import glob
@@ -485,8 +596,8 @@ def write_traffic(fetch_dir, write_dir, workload, fmt="int4"):
     fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
     kname = "kv4::decode_split_kernel<128, 4, %d>" % FORMATS[fmt]
     pick = lambda vals: next(v for k, v in vals.items() if kname in k)
-    copy_f = max(v for k, vs in fetch.items() if "copyBuffer" in k for v in vs)
-    copy_w = max(v for k, vs in write.items() if "copyBuffer" in k for v in vs)
+    copy_f = max(v for k, vs in fetch.items() if "probe_copy_kernel" in k for v in vs)
+    copy_w = max(v for k, vs in write.items() if "probe_copy_kernel" in k for v in vs)
     n = 1 << 30
     ff, wf = n / (copy_f * 1024), n / (copy_w * 1024)
     f_kib, w_kib = pick(fetch), pick(write)
@@ -498,23 +609,46 @@ def write_traffic(fetch_dir, write_dir, workload, fmt="int4"):
             rec = json.load(f)
     except (OSError, ValueError):
         rec = {}
-    cmd = ("rocprofv3 --pmc %s --kernel-include-regex 'kv4|copyBuffer|copy' --output-format csv -d %s -o run -- "
-           "python bench.py --workload %s --steps 4 --warmup 1 --baselines '' --no-cpu-baseline --no-quality "
-           "--copy-calibration")
+    cmd = ("rocprofv3 --pmc %s --kernel-include-regex 'decode_split|probe_copy' --output-format csv -d %s -o run -- "
+           "python bench.py --workload %s --steps 2 --warmup 1 --decode-launches 8 --extras none --copy-calibration")
     rec["%s/%s" % (workload, fmt)] = {
-        "kernel": "decode_split_kernel<128,4,%s>" % {"int4": "INT4_PROT", "int8": "INT8", "bf16": "BF16"}[fmt],
+        "kernel": KERNELS[fmt],
         "kernel_source_hash": kernel_source_hash(),
         "bytes_per_launch": fb + wb, "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
         "fetch_size_kib_mean": sum(f_kib) / len(f_kib), "write_size_kib_mean": sum(w_kib) / len(w_kib),
         "dispatches": len(f_kib),
-        "copy_reference": {"bytes_read": n, "bytes_written": n, "fetch_size_kib": copy_f, "write_size_kib": copy_w,
-                           "fetch_factor": ff, "write_factor": wf},
+        "copy_reference": {"kernel": "kv4::probe_copy_kernel", "bytes_read": n, "bytes_written": n,
+                           "fetch_size_kib": copy_f, "write_size_kib": copy_w, "fetch_factor": ff,
+                           "write_factor": wf},
         "commands": [cmd % ("FETCH_SIZE", fetch_dir, workload), cmd % ("WRITE_SIZE", write_dir, workload),
                      "python bench.py --workload %s --traffic-from %s %s" % (workload, fetch_dir, write_dir)],
     }
     with open(path, "w") as f:
         json.dump(rec, f, indent=1)
     return rec["%s/%s" % (workload, fmt)]
+
+
+def copy_calibration(device):
+    """One 1 GiB probe copy: the reference dispatch for the PMC byte counters."""
+    import torch
+    import int4_kv_cache_fwht_amd as kv4
+    n = 1 << 30
+    a = torch.ones(n, dtype=torch.uint8, device=device)
+    b = torch.empty_like(a)
+    ms = kv4.hbm_probe(1, a, b, n, 1)[0]
+    del a, b
+    torch.cuda.empty_cache()
+    return 2 * n / (ms * 1e-3) / 1e9
+
+
+def workload_config(w, layers, n_caches, fmt="int4"):
+    return {"workload": w.name, "batch": w.batch, "layers_per_step": layers, "kv_heads": w.num_kv_heads,
+            "q_heads": w.num_q_heads, "head_dim": w.head_dim,
+            "context": "%s%s" % (w.lengths_kind, list(w.length_args)), "sinks": w.num_sinks,
+            "recent": w.num_recent, "hadamard_block": w.hadamard_block,
+            "kv_storage": {"int4": "int4 pages + int8 sink/recent", "int8": "int8 pages",
+                           "bf16": "bf16 pages"}[fmt],
+            "distinct_caches": n_caches, "seed": w.seed}
 
 
 def main():
@@ -526,31 +660,52 @@ def main():
         print("bench.py runs on exactly one GPU: the decode path is built and measured on one GPU "
               "(multi-GPU sharding is not built); use --gpus 1", file=sys.stderr)
         sys.exit(2)
+    import dataclasses
     import torch
     import kv4_inputs as W
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     device = torch.device("cuda", 0)
     if args.workload == "append":
-        print(json.dumps(append_workload(device)), flush=True)
+        rec = append_workload(device)
+        print(json.dumps({"metric": "INT4 KV append (rotation + quantization + pack) tokens/s",
+                          "value": rec["tokens_per_s_b128"], "unit": "tokens/s", "n_gpus": 1, "steps": 512,
+                          "warmup": 1, "ms_per_step": rec["append_step_us"]["b128"] * 1e-3, "higher_is_better": True,
+                          "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+                          "config": dict(rec["config"], workload="append"), "append": rec}), flush=True)
         return
     if args.workload == "multi_query":
         print(json.dumps(mq_workload(device, args.mq_rows, args.steps, args.warmup)), flush=True)
         return
     w = W.WORKLOADS[args.workload]
     if args.hadamard_block:
-        import dataclasses
         w = dataclasses.replace(w, hadamard_block=args.hadamard_block)
-    total = args.warmup + args.steps + 12
+    layers = args.layers or w.layers
+    n_caches = args.caches or max(layers, 4)
 
-    print("bench: building %d int4 caches for %s" % (args.caches, w.name), file=sys.stderr, flush=True)
-    b = Bench(w, "int4", args.caches, total, device, args.decode_waves)
+    log("building %d int4 layer caches for %s (%d layers per step)" % (n_caches, w.name, layers))
+    b = Bench(w, "int4", n_caches, layers, args.warmup + args.steps + 2, device, args.decode_waves)
     for _ in range(args.warmup):
         b.step()
     el, toks = b.timed(args.steps)
-    split_s, merge_s, append_s, bytes_per_launch = b.profiled(12)
-    achieved = bytes_per_launch / split_s / 1e9
+    log("timed %d steps in %.3f s" % (args.steps, el))
+    prof = b.profiled_steps(2)
+    split, merge, bytes_launch = b.decode_only(args.decode_launches)
+    b.close()
+    del b
+    torch.cuda.empty_cache()
+    st = stats_us(split)
+    achieved = bytes_launch / (st["mean"] * 1e-6) / 1e9
     traffic = measured_traffic(w.name, "int4")
-    kvtok_step = toks / args.steps
+    layer_wall_us = el / (args.steps * layers) * 1e6
+    kern = {"append": stats_us(prof["append"])["mean"], "decode_split": stats_us(prof["split"])["mean"],
+            "decode_merge": stats_us(prof["merge"])["mean"]}
+    kern_sum = sum(kern.values())
+    # the kernels of one stream cannot take longer than the wall clock around them; a violation
+    # means the events over-count (seen under a kernel tracer, which lengthens short kernels)
+    events_ok = kern_sum <= layer_wall_us
+    if not events_ok:
+        log("warning: kernel events per layer (%.1f us) exceed the wall-clock layer step (%.1f us)" % (
+            kern_sum, layer_wall_us))
     result = {
         "metric": METRIC,
         "value": toks / el,
@@ -562,45 +717,64 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": DTYPE,
         "data": "synthetic",
-        "config": {"workload": w.name, "batch": w.batch, "kv_heads": w.num_kv_heads, "q_heads": w.num_q_heads,
-                   "head_dim": w.head_dim, "context": "%s%s" % (w.lengths_kind, list(w.length_args)),
-                   "sinks": w.num_sinks, "recent": w.num_recent, "hadamard_block": w.hadamard_block,
-                   "kv_storage": "int4 pages + int8 sink/recent", "distinct_caches": args.caches,
-                   "kv_tokens_per_step": kvtok_step},
+        "config": dict(workload_config(w, layers, n_caches), kv_tokens_per_step=toks / args.steps),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                     "kernel": "decode_split_kernel<128,4,INT4_PROT>", "avg_launch_us": split_s * 1e6,
-                     "algorithmic_bytes_per_launch": bytes_per_launch},
-        "step_breakdown_us": {"append": append_s * 1e6, "decode_split": split_s * 1e6, "decode_merge": merge_s * 1e6},
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic, "kernel": KERNELS["int4"],
+                     "avg_launch_us": st["mean"], "median_launch_us": st["median"], "min_launch_us": st["min"],
+                     "max_launch_us": st["max"], "launches": st["launches"],
+                     "timing": "kernel-stamped HIP events of %d back-to-back decode-only launches cycling the %d "
+                               "layer caches" % (st["launches"], n_caches),
+                     "algorithmic_bytes_per_launch": bytes_launch},
+        "step_breakdown_us": {"per_layer": kern, "kernels_sum_per_layer": kern_sum, "wall_per_layer": layer_wall_us,
+                              "per_step_kernels": kern_sum * layers, "kernels_within_wall": events_ok},
     }
-    del b
-    torch.cuda.empty_cache()
-
-    base = {}
-    for fmt in [f for f in args.baselines.split(",") if f]:
-        print("bench: baseline %s" % fmt, file=sys.stderr, flush=True)
-        bb = Bench(w, fmt, args.caches, args.warmup + 2 * args.baseline_steps, device, args.decode_waves)
-        for _ in range(args.warmup):
-            bb.step()
-        el2, toks2 = bb.timed(args.baseline_steps)
-        s2, m2, a2, by2 = bb.profiled(args.baseline_steps)
-        ach2 = by2 / s2 / 1e9
-        base[fmt] = {"kv_tokens_per_s": toks2 / el2, "ms_per_step": el2 / args.baseline_steps * 1e3,
-                     "split_avg_us": s2 * 1e6, "achieved_GBps": ach2, "frac": ach2 / HBM_PEAK_GBPS,
-                     "int4_speedup": (toks / el) / (toks2 / el2)}
-        del bb
-        torch.cuda.empty_cache()
-    if base:
+    ex = args.extras
+    if "probe" in ex:
+        log("HBM probe")
+        pr = hbm_probe(device)
+        result["roofline"]["probe"] = pr
+        result["roofline"]["frac_of_probe_read"] = achieved / pr["read_GBps"]
+    if "baselines" in ex:
+        base = {}
+        for fmt in [f for f in args.baselines.split(",") if f]:
+            log("baseline %s (%d caches cycled)" % (fmt, args.baseline_caches))
+            r = run_decode_workload(w, fmt, args.baseline_caches, layers, max(args.steps // 2, 4), 1,
+                                    args.decode_launches, device, args.decode_waves)
+            r["int4_speedup_kv_tokens"] = result["value"] / r["kv_tokens_per_s"]
+            r["int4_split_speedup"] = r["split_us"]["mean"] / st["mean"]
+            r["kernel"] = KERNELS[fmt]
+            r["distinct_caches"] = args.baseline_caches
+            base[fmt] = r
         result["baselines"] = base
+    if "workloads" in ex:
+        wl = {}
+        for name in ("qwen3_8b_layer", "long_context"):
+            if name == w.name:
+                continue
+            log("workload %s" % name)
+            w2 = W.WORKLOADS[name]
+            r = run_decode_workload(w2, "int4", 4, 1, 12, 2, 64, device, args.decode_waves)
+            r["config"] = workload_config(w2, 1, 4)
+            r["traffic"] = measured_traffic(name, "int4")
+            if "probe" in result["roofline"]:
+                r["frac_of_probe_read"] = r["achieved_GBps"] / result["roofline"]["probe"]["read_GBps"]
+            wl[name] = r
+        result["workloads"] = wl
+    if "append" in ex:
+        log("append workload")
+        result["append"] = append_workload(device)
+    if "protection" in ex:
+        log("protection cost")
+        result["protection_cost"] = protection_cost(device)
     if args.copy_calibration:
-        result["copy_probe_GBps"] = copy_probe(device)
-    if not args.no_quality:
-        print("bench: quality diagnostic", file=sys.stderr, flush=True)
-        result["quality"] = quality(w, device)
-    if not args.no_cpu_baseline:
-        print("bench: cpu baseline", file=sys.stderr, flush=True)
+        result["copy_calibration_GBps"] = copy_calibration(device)
+    if "quality" in ex:
+        log("quality diagnostic")
+        result["quality"] = quality(W.WORKLOADS["qwen3_8b_layer"], device)
+    if "cpu" in ex:
+        log("cpu baseline")
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_baseline_seconds, device)
     print(json.dumps(result), flush=True)
 

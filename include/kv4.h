@@ -277,6 +277,25 @@ typedef struct kv4_profile {
 } kv4_profile;
 kv4_status kv4_profile_enable(kv4_cache_t h, int32_t enable);
 kv4_status kv4_profile_read(kv4_cache_t h, kv4_profile* out);
+/* Per-launch durations (ms, launch order) of one kernel kind since profiling was enabled: kind 0
+ * append, 1 decode split, 2 decode merge, 3 multi-query split, 4 multi-query merge.  Writes up to
+ * cap values to ms (host) and the number collected to *n.  Waits for the events. */
+kv4_status kv4_profile_durations(kv4_cache_t h, int32_t kind, float* ms, int32_t cap, int32_t* n);
+
+/*
+ * HBM ceiling probe (measurement; no cache involved): the practical streaming bandwidth of the
+ * device that the cache kernels' achieved bytes per second are compared with, beside the published
+ * peak.  Runs `reps` back-to-back launches on `stream` of
+ *   mode 0: a streaming read of `bytes` from src (16-byte loads); each lane of the grid stores one
+ *           folded word to dst, so dst (device) must hold blocks * 1024 bytes;
+ *   mode 1: a copy of `bytes` from src to dst (device, non-overlapping);
+ * each launch stamping its own start / stop events, waits for them and writes each launch's
+ * duration in ms to ms[0 .. reps) (host).  blocks: workgroups of 256 lanes, 0 = 8 per compute unit.
+ * bytes must be a positive multiple of 16, pointers 16-byte aligned, on the current device.
+ * Errors: INVALID_ARGUMENT, HIP.
+ */
+kv4_status kv4_hbm_probe(int32_t mode, const void* src, void* dst, size_t bytes, int32_t blocks, int32_t reps,
+                         float* ms, void* stream /* hipStream_t */);
 
 const char* kv4_status_string(kv4_status s);
 /* Detail of the last error on h (or of the last handle-less error when h is NULL). */

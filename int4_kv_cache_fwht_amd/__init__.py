@@ -20,9 +20,11 @@ from ._binding import (  # noqa: F401
     lib,
     lib_path,
     kv4_buffer_sizes_query,
+    hbm_probe,
 )
 
 lib()  # load now: a missing library fails the import, never a silent fallback
 
 __all__ = ["KV4Error", "Config", "BufferSizes", "Cache", "FORMAT_INT4_PROT", "FORMAT_INT8", "FORMAT_BF16",
-           "EVICT_DUAL_WRITE", "EVICT_REQUANT", "STATUS", "lib", "lib_path", "kv4_buffer_sizes_query"]
+           "EVICT_DUAL_WRITE", "EVICT_REQUANT", "STATUS", "lib", "lib_path", "kv4_buffer_sizes_query",
+           "hbm_probe"]

@@ -125,6 +125,8 @@ def lib():
         L.kv4_set_decode_waves.argtypes = [P, I32]
         L.kv4_profile_enable.argtypes = [P, I32]
         L.kv4_profile_read.argtypes = [P, P]
+        L.kv4_profile_durations.argtypes = [P, I32, P, I32, P]
+        L.kv4_hbm_probe.argtypes = [I32, P, P, SZ, I32, I32, P, P]
         L.kv4_status_string.argtypes = [ctypes.c_int]
         L.kv4_status_string.restype = ctypes.c_char_p
         L.kv4_last_error.argtypes = [P]
@@ -134,7 +136,7 @@ def lib():
                      "kv4_decode_attention_bf16", "kv4_decode_attention_noalloc",
                      "kv4_multi_query_workspace_size", "kv4_multi_query_attention",
                      "kv4_seq_length", "kv4_block_table", "kv4_free_pages", "kv4_set_decode_waves",
-                     "kv4_profile_enable", "kv4_profile_read"):
+                     "kv4_profile_enable", "kv4_profile_read", "kv4_profile_durations", "kv4_hbm_probe"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -157,6 +159,25 @@ def kv4_buffer_sizes_query(cfg: Config) -> BufferSizes:
     _check(lib().kv4_buffer_sizes_query(ctypes.byref(c), ctypes.byref(out)))
     return BufferSizes(out.page_pool, out.int8_pool, out.block_table, out.page_block_bytes, out.int8_tile_bytes,
                        out.int8_tiles)
+
+
+def hbm_probe(mode: int, src: torch.Tensor, dst: torch.Tensor, nbytes: int, reps: int, blocks: int = 0,
+              stream=None):
+    """kv4_hbm_probe: per-launch durations (ms) of `reps` streaming reads (mode 0) or copies (mode 1)
+    of `nbytes` from src to dst (device tensors of the current device)."""
+    if src.device.type != "cuda" or dst.device.type != "cuda":
+        raise ValueError("probe buffers must be device tensors")
+    if src.numel() * src.element_size() < nbytes:
+        raise ValueError("src smaller than nbytes")
+    if blocks <= 0:
+        blocks = 8 * torch.cuda.get_device_properties(dst.device).multi_processor_count
+    need = nbytes if mode == 1 else blocks * 1024
+    if dst.numel() * dst.element_size() < need:
+        raise ValueError("dst too small")
+    ms = (ctypes.c_float * reps)()
+    _check(lib().kv4_hbm_probe(int(mode), src.data_ptr(), dst.data_ptr(), int(nbytes), int(blocks), int(reps), ms,
+                               _stream_ptr(stream)))
+    return [ms[i] for i in range(reps)]
 
 
 def _stream_ptr(stream) -> Optional[int]:
@@ -382,6 +403,15 @@ class Cache:
 
     def profile_enable(self, enable: bool = True):
         _check(lib().kv4_profile_enable(self._h, 1 if enable else 0), self._h)
+
+    def profile_durations(self, kind: str) -> list:
+        """Per-launch durations (ms) since profile_enable: 'append', 'split', 'merge', 'mq_split', 'mq_merge'."""
+        k = ["append", "split", "merge", "mq_split", "mq_merge"].index(kind)
+        n = ctypes.c_int32()
+        _check(lib().kv4_profile_durations(self._h, k, None, 0, ctypes.byref(n)), self._h)
+        buf = (ctypes.c_float * max(n.value, 1))()
+        _check(lib().kv4_profile_durations(self._h, k, buf, n.value, ctypes.byref(n)), self._h)
+        return [buf[i] for i in range(n.value)]
 
     def profile_read(self) -> dict:
         p = _Profile()

@@ -86,6 +86,7 @@ struct Profiler {
     std::vector<std::vector<hipEvent_t>> decode_ev; // {split start, split stop, merge start, merge stop}
     std::vector<std::vector<hipEvent_t>> mq_ev;     // the same for multi-query calls
     kv4_profile totals{};
+    std::vector<float> durations[5]; // per launch, in launch order: append, split, merge, mq split, mq merge
 
     // Timing-only events (no system-scope fence). Each launch stamps its own start/stop pair from
     // its dispatch, so an interval is one kernel's execution, as a kernel trace reports it.
@@ -113,6 +114,7 @@ struct Profiler {
         decode_ev.clear();
         mq_ev.clear();
         totals = kv4_profile{};
+        for (auto& d : durations) d.clear();
     }
     hipError_t collect()
     {
@@ -123,6 +125,7 @@ struct Profiler {
             hipEventElapsedTime(&ms, v[0], v[1]);
             totals.append_launches += 1;
             totals.append_ms += ms;
+            durations[0].push_back(ms);
             for (auto e : v) hipEventDestroy(e);
         }
         append_ev.clear();
@@ -135,6 +138,8 @@ struct Profiler {
             totals.decode_launches += 1;
             totals.split_ms += a;
             totals.merge_ms += b;
+            durations[1].push_back(a);
+            durations[2].push_back(b);
             for (auto e : v) hipEventDestroy(e);
         }
         decode_ev.clear();
@@ -147,6 +152,8 @@ struct Profiler {
             totals.mq_launches += 1;
             totals.mq_split_ms += a;
             totals.mq_merge_ms += b;
+            durations[3].push_back(a);
+            durations[4].push_back(b);
             for (auto e : v) hipEventDestroy(e);
         }
         mq_ev.clear();
@@ -820,6 +827,44 @@ kv4_status kv4_profile_read(kv4_cache_t h, kv4_profile* out)
     if (e != hipSuccess) return hip_fail(h, e, "profiling events");
     *out = h->prof.totals;
     return KV4_OK;
+}
+
+kv4_status kv4_profile_durations(kv4_cache_t h, int32_t kind, float* ms, int32_t cap, int32_t* n)
+{
+    if (!h || !n || kind < 0 || kind > 4 || cap < 0 || (cap > 0 && !ms))
+        return fail(h, KV4_ERR_INVALID_ARGUMENT, "bad argument");
+    DeviceGuard g(h->device);
+    hipError_t e = h->prof.collect();
+    if (e != hipSuccess) return hip_fail(h, e, "profiling events");
+    const std::vector<float>& d = h->prof.durations[kind];
+    for (size_t i = 0; i < d.size() && i < (size_t)cap; i++) ms[i] = d[i];
+    *n = (int32_t)d.size();
+    return KV4_OK;
+}
+
+kv4_status kv4_hbm_probe(int32_t mode, const void* src, void* dst, size_t bytes, int32_t blocks, int32_t reps,
+                         float* ms, void* stream)
+{
+    if ((mode != 0 && mode != 1) || !src || !dst || bytes == 0 || bytes % 16 || ((uintptr_t)src % 16) ||
+        ((uintptr_t)dst % 16) || reps < 1 || !ms || blocks < 0)
+        return fail(nullptr, KV4_ERR_INVALID_ARGUMENT, "bad probe argument");
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(nullptr, e, "device query");
+    if (blocks == 0) blocks = 8 * (cus > 0 ? cus : 256);
+    hipStream_t strm = (hipStream_t)stream;
+    std::vector<hipEvent_t> ev;
+    e = Profiler::make(2 * reps, &ev);
+    kv4_status st = KV4_OK;
+    for (int r = 0; r < reps && e == hipSuccess; r++)
+        e = kv4::launch_probe(mode, src, dst, (uint64_t)bytes, blocks, strm, kv4::KernelTimer{ev[2 * r], ev[2 * r + 1]});
+    if (e == hipSuccess) e = hipEventSynchronize(ev[2 * reps - 1]);
+    for (int r = 0; r < reps && e == hipSuccess; r++) e = hipEventElapsedTime(&ms[r], ev[2 * r], ev[2 * r + 1]);
+    if (e != hipSuccess) st = hip_fail(nullptr, e, "probe");
+    for (auto x : ev)
+        if (x) hipEventDestroy(x);
+    return st;
 }
 
 } // extern "C"

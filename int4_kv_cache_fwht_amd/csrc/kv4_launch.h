@@ -107,5 +107,9 @@ hipError_t launch_mq_split(int d, int g, int format, const MqArgs& a, hipStream_
                            const KernelTimer& tm = KernelTimer{});
 hipError_t launch_mq_merge(int d, int g, const MqArgs& a, hipStream_t stream, const KernelTimer& tm = KernelTimer{});
 hipError_t mq_split_residency(int d, int g, int format, int* blocks_per_cu);
+// HBM probes (measurement only): mode 0 streams `bytes` from src and writes one word per lane of
+// the grid to dst (blocks * 256 words); mode 1 copies src to dst.  bytes is a multiple of 16.
+hipError_t launch_probe(int mode, const void* src, void* dst, uint64_t bytes, int blocks, hipStream_t stream,
+                        const KernelTimer& tm = KernelTimer{});
 
 } // namespace kv4

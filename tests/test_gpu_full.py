@@ -48,7 +48,7 @@ def _gpu_codes(cache, pool, i8, seq, t, h, kv):
 def _check_workload(name, sample_fn, positions_per_seq=12, mq_rows=(4,)):
     w = W.WORKLOADS[name]
     dev = torch.device("cuda", 0)
-    b = bench.Bench(w, "int4", 1, 2, dev, 0)
+    b = bench.Bench(w, "int4", 1, 1, 2, dev, 0)
     b.step()                       # append 1 position to every sequence, decode all (auto split)
     torch.cuda.synchronize()
     out = b.out.cpu().numpy().astype(np.float64)
