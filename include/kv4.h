@@ -260,6 +260,10 @@ kv4_status kv4_free_pages(kv4_cache_t h, int32_t* n);
 
 /* Tuning: number of waves the decode split kernel launches (0 = automatic). */
 kv4_status kv4_set_decode_waves(kv4_cache_t h, int32_t waves);
+/* Tuning: a second round of round2_waves decode split waves that share the last
+ * (1000 - round1_permille) / 1000 of the call's steps (0 = one round).  The results do not depend
+ * on it beyond rounding order. */
+kv4_status kv4_set_decode_rounds(kv4_cache_t h, int32_t round2_waves, int32_t round1_permille);
 
 /* Kernel timing (measurement of the hot path).  When enabled, each kernel a call launches on its
  * stream stamps a pair of HIP events from its own dispatch (start, stop), so a duration is that

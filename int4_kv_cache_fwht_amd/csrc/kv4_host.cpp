@@ -2,6 +2,7 @@
 // the per-call plans to the device and kernel launches.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -175,6 +176,8 @@ struct kv4_cache {
     int resident_waves = 2048; // decode split waves resident at once on the device
     int mq_resident_waves = 2048; // multi-query split waves resident at once
     int decode_waves = 0; // 0: automatic
+    int round2_waves = 0; // decode split: waves of a second round (0: one round)
+    int round1_permille = 1000; // share of the steps in the first round when there is a second
     float cb = 1.0f;
     void* scratch = nullptr;                // this device's decode scratch (kDecodeScratchBytes)
     std::vector<kv4::DecodeUnit> units_buf; // decode plan, reused (capacity for kArgEntries entries)
@@ -584,6 +587,18 @@ kv4_status decode_impl(kv4_cache_t h, int32_t n_seqs, const int32_t* seq_ids, co
     int64_t W = h->decode_waves > 0 ? h->decode_waves : auto_waves(h, total);
     if (W > total) W = total;
     if (W < 1) W = 1;
+    // optional second round: W2 more waves share the last (1000 - round1_permille) / 1000 of the
+    // steps, when both rounds hold at least one step per wave
+    const int64_t W1 = W;
+    int64_t T1 = total;
+    if (h->round2_waves > 0 && h->round1_permille < 1000) {
+        const int64_t W2 = std::min<int64_t>(h->round2_waves, wmax - W1);
+        const int64_t t1 = total * h->round1_permille / 1000;
+        if (W2 > 0 && t1 >= W1 && total - t1 >= W2) {
+            T1 = t1;
+            W = W1 + W2;
+        }
+    }
     const int64_t n_units = (int64_t)units.size();
     if (noalloc) {
         workspace = h->scratch;
@@ -629,6 +644,8 @@ kv4_status decode_impl(kv4_cache_t h, int32_t n_seqs, const int32_t* seq_ids, co
     a.part_o = (float*)(ws + align_up(ubytes) + align_up((size_t)parts * G * 2 * sizeof(float)));
     a.out = out;
     a.total_steps = total;
+    a.steps1 = T1;
+    a.n_waves1 = (int)W1;
     a.page_block = (int64_t)h->sizes.page_block;
     a.int8_tile = (int64_t)h->sizes.int8_tile;
     a.n_units = (int)n_units;
@@ -807,6 +824,15 @@ kv4_status kv4_set_decode_waves(kv4_cache_t h, int32_t waves)
 {
     if (!h || waves < 0) return fail(h, KV4_ERR_INVALID_ARGUMENT, "bad argument");
     h->decode_waves = waves;
+    return KV4_OK;
+}
+
+kv4_status kv4_set_decode_rounds(kv4_cache_t h, int32_t round2_waves, int32_t round1_permille)
+{
+    if (!h || round2_waves < 0 || round1_permille < 1 || round1_permille > 1000)
+        return fail(h, KV4_ERR_INVALID_ARGUMENT, "bad argument");
+    h->round2_waves = round2_waves;
+    h->round1_permille = round1_permille;
     return KV4_OK;
 }
 

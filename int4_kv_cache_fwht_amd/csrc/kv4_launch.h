@@ -52,9 +52,12 @@ struct DecodeArgs {
     float* part_o;            // [(W + n_units)][G][D]
     float* out;               // fp32 [entries][hq][D]
     int64_t total_steps;
+    // two rounds of waves: waves [0, n_waves1) share the first steps1 global steps, waves
+    // [n_waves1, n_waves) the rest (one round: n_waves1 = n_waves, steps1 = total_steps)
+    int64_t steps1;
     int64_t page_block;
     int64_t int8_tile;
-    int n_units, n_waves;
+    int n_units, n_waves, n_waves1;
     int hkv, max_pps, sinks, recent, block, int8_tiles;
     float cb;         // fl32(1/sqrt(block))
     float scale_log2; // softmax scale * log2(e)

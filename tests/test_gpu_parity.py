@@ -201,3 +201,24 @@ def test_decode_wave_counts():
         err = np.abs(out - ref).max()
         print("waves", waves, "max-abs", err, flush=True)
         assert err <= TOL
+
+
+def test_decode_two_rounds():
+    """A second round of split waves over the last share of the steps (hardware-balanced tail): the
+    partition into rounds changes nothing beyond rounding order; round-2 slices shorter than a unit,
+    longer than a unit, and a round 2 with more waves than round 1."""
+    _print_case("two rounds")
+    hq, hkv, d = 32, 8, 128
+    lens = [1, 17, 100, 132, 133, 300, 1000, 4000]
+    p = Pair(hq, hkv, d, num_pages=2048, max_seqs=16, max_pps=300, S=4, R=128, b=128)
+    ks, vs = zip(*[_kv(L, hkv, d, seed=3, idx=i) for i, L in enumerate(lens)])
+    p.append(list(range(len(lens))), lens, torch.cat(ks).contiguous(), torch.cat(vs).contiguous())
+    q = W.queries(len(lens), hq, d, seed=17, step=0, device="cuda")
+    ids = list(range(len(lens)))
+    for waves, w2, pm in ((13, 7, 500), (64, 256, 850), (0, 512, 900), (0, 2048, 700), (1, 3, 999)):
+        p.gpu.set_decode_waves(waves)
+        p.gpu.set_decode_rounds(w2, pm)
+        out, ref = p.decode(ids, q)
+        err = np.abs(out - ref).max()
+        print("waves", waves, "round 2", w2, "permille", pm, "max-abs", err, flush=True)
+        assert err <= TOL
