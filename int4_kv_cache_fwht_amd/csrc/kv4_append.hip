@@ -38,18 +38,15 @@ __device__ __forceinline__ void fwht_in_lane(float (&y)[N], int b)
     }
 }
 
-// Last stage h = N when b == 2N: partner lane holds the other half of the row.
+// The stage whose pairs span the lane pair: the partner lane holds the other value of each pair.
+// Half 0 (dim i) takes own + partner, half 1 (dim i + span) partner - own: one DPP move and one
+// fma with a factor of +-1 per value (rounded once, like the add or subtract it replaces).
 template <int N>
 __device__ __forceinline__ void fwht_across_pair(float (&y)[N], int half)
 {
-    const uint32_t sgn = half ? 0x80000000u : 0u;
+    const float sgn = half ? -1.f : 1.f;
 #pragma unroll
-    for (int i = 0; i < N; i++) {
-        float own = y[i];
-        float partner = dpp_xor1(own);
-        // half 0: own(dim i) + partner(dim i+N); half 1: partner(dim i) - own(dim i+N)
-        y[i] = partner + as_float(as_uint(own) ^ sgn);
-    }
+    for (int i = 0; i < N; i++) y[i] = butterfly_xor<1>(y[i], sgn);
 }
 
 struct QuantParams {
