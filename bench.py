@@ -464,22 +464,39 @@ def append_workload(device, repeats=7):
                     "repeats of (mean over the 512 step launches) and of the prefill launch" % repeats}
 
 
-def protection_cost(device, launches=48, n_caches=4):
+def protection_cost(device, rounds=6, launches=8, n_caches=4):
     """Decode split time and algorithmic bytes on the Qwen3-8B layer with no protection, sinks only,
-    recent window only and both (INT4 + INT8 protection), b = 128."""
+    recent window only and both (INT4 + INT8 protection), b = 128.  The four variants' caches are
+    built first and their decode-only launches interleaved (rounds x launches each), so that a
+    drift of the device's speed during the run falls on all of them alike."""
+    import torch
     import kv4_inputs as W
     w = W.WORKLOADS["qwen3_8b_layer"]
+    variants = ((0, 0), (4, 0), (0, 128), (4, 128))
+    benches = {v: Bench(w, "int4", n_caches, 1, 2, device, 0, sinks=v[0], recent=v[1]) for v in variants}
+    split = {v: [] for v in variants}
+    nbytes = {}
+    for _ in range(rounds):
+        for v in variants:
+            sp, _, by = benches[v].decode_only(launches)
+            split[v] += sp
+            nbytes[v] = by
+    for b in benches.values():
+        b.close()
+    torch.cuda.empty_cache()
     out = {}
-    for S, R in ((0, 0), (4, 0), (0, 128), (4, 128)):
-        r = run_decode_workload(w, "int4", n_caches, 1, 4, 1, launches, device, sinks=S, recent=R)
-        out["S%d_R%d" % (S, R)] = {"split_us": r["split_us"]["mean"], "split_us_median": r["split_us"]["median"],
-                                   "algorithmic_bytes_per_launch": r["algorithmic_bytes_per_launch"],
-                                   "achieved_GBps": r["achieved_GBps"], "frac": r["frac"]}
+    for (S, R) in variants:
+        st = stats_us(split[(S, R)])
+        by = nbytes[(S, R)]
+        out["S%d_R%d" % (S, R)] = {"split_us": st["mean"], "split_us_median": st["median"],
+                                   "algorithmic_bytes_per_launch": by, "achieved_GBps": by / (st["mean"] * 1e-6) / 1e9,
+                                   "frac": by / (st["mean"] * 1e-6) / 1e9 / HBM_PEAK_GBPS}
     base = out["S0_R0"]
     for v in out.values():
         v["time_vs_unprotected"] = v["split_us"] / base["split_us"] - 1.0
         v["bytes_vs_unprotected"] = v["algorithmic_bytes_per_launch"] / base["algorithmic_bytes_per_launch"] - 1.0
-    return {"workload": "qwen3_8b_layer", "launches": launches, "variants": out}
+    return {"workload": "qwen3_8b_layer", "launches_per_variant": rounds * launches, "order": "interleaved",
+            "variants": out}
 
 
 def mq_workload(device, n_q, steps, warmup, n_caches=4):

@@ -189,7 +189,12 @@ kv4_status kv4_seq_free(kv4_cache_t h, int32_t seq_id);
 kv4_status kv4_decode_workspace_size(kv4_cache_t h, int32_t n_seqs, size_t* bytes);
 
 /*
- * Decode attention for n_seqs sequences (ids distinct, every length L >= 1):
+ * Decode attention for n_seqs sequences (ids distinct, every length L >= 1).  [SAW] Abstract:
+ * attention fused over the paged INT4 layout of block-Hadamard-rotated keys and values (the query
+ * is rotated once and the output un-rotated once, since H is orthogonal); [KV4] Abstract and
+ * [TOP5]: the attention-sink and recent-context positions are read from their INT8 copies, every
+ * other position from INT4.
+ *
  *   q   (device) bf16 [n_seqs][Hq][D], row i for seq_ids[i];
  *   out (device) fp32 [n_seqs][Hq][D].
  * Query head g reads kv head g / G.  Over all L positions t (the INT8 slot when t is in Prot(L),
