@@ -262,12 +262,13 @@ size_t decode_ws_bytes(const kv4_cache* h, int64_t n_units, int64_t waves)
            align_up((size_t)parts * G * D * sizeof(float));
 }
 
-// Multi-query split tasks: three rounds of resident waves when no (sequence, kv head) has more
-// than 4 row tiles of kMqRows query rows, two rounds otherwise.  Smaller chunks balance the waves
-// of the few-tile calls; with many tiles per chunk they only add partials and re-reads (Qwen3-8B
-// layer on MI355X: 16 rows per sequence 336 against 372 us, 4 rows 127 against 132 us, 64 rows
-// 1196 us with two rounds against 1393 us with three).  n_q is read only where it is positive;
-// the call validates it.
+// Multi-query split tasks, in rounds of resident waves by the most row tiles (of kMqRows query rows)
+// any (sequence, kv head) has: two rounds at one tile, three at two to four, two above.  Smaller
+// chunks balance the waves of the few-tile calls, but each adds a partial per row tile; with one
+// tile the merge's share decides, with many tiles per chunk they only add partials and re-reads.
+// Qwen3-8B layer on MI355X (split + merge): 4 rows per sequence (one tile) 114 us with two rounds
+// against 118 with three; 16 rows 318 against 345 with two; 64 rows 1196 us with two rounds
+// against 1393 us with three.  n_q is read only where it is positive; the call validates it.
 int64_t mq_target_tasks(const kv4_cache* h, int32_t n_seqs, const int32_t* n_q)
 {
     const int G = h->st.cfg.hq / h->st.cfg.hkv;
@@ -275,7 +276,7 @@ int64_t mq_target_tasks(const kv4_cache* h, int32_t n_seqs, const int32_t* n_q)
     if (n_q)
         for (int32_t i = 0; i < n_seqs; i++)
             if (n_q[i] > 0) tiles = std::max<int64_t>(tiles, ((int64_t)n_q[i] * G + kv4::kMqRows - 1) / kv4::kMqRows);
-    return (tiles <= 4 ? 3 : 2) * (int64_t)h->mq_resident_waves;
+    return (tiles >= 2 && tiles <= 4 ? 3 : 2) * (int64_t)h->mq_resident_waves;
 }
 
 size_t mq_ws_bytes(const kv4_cache* h, const kv4::MqPlan& p)

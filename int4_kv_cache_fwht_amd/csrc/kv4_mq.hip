@@ -34,6 +34,18 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 
 constexpr float kMqTau = 1.f;
 constexpr float kPScale = 134217728.f; // 2^27
+// INT4 steps are staged in LDS: each step's two page blocks are copied by global_load_lds_dwordx4
+// (no VGPRs while in flight) into a ring of kMqStages stage buffers per wave, kMqStages - 1 steps
+// ahead of the step being computed.
+constexpr int kMqStages = 3;
+
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding: vmcnt bits 3:0 and 15:14)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x0F70);
+}
 
 template <typename T>
 __device__ __forceinline__ T mq_uniform(const T* p)
@@ -173,6 +185,9 @@ struct MqWave {
     static constexpr int DPL = D / 4;   // query dims per lane in the prologue
     static constexpr int QT = kMqRows / G;
     static constexpr int IB = 16 * D + 128; // bytes of an INT4 page block / an INT8 tile block
+    static constexpr int CPB = (IB + 1023) / 1024; // 1 KB copy instructions per page block
+    static constexpr int SB = 1024 * CPB;          // LDS bytes of a staged page block (padded)
+    static constexpr int STAGE = 2 * SB;           // LDS bytes of one staged INT4 step (two blocks)
 
     // One step's operands for this lane.  INT8 buffers hold twice the key and value bytes.
     template <bool IS8>
@@ -194,6 +209,7 @@ struct MqWave {
     uint32_t pstride;     // bytes from one page to the next (all kv heads' blocks)
     int p0, p1;          // INT4 page range (INT4_PROT) or page count (INT8 format: p1)
     float m_ref = -__builtin_inff(), lsum = 0.f, zsum = 0.f, Ar = 0.f, Br = 0.f;
+    __attribute__((address_space(3))) uint8_t* ring; // this wave's kMqStages INT4 stage buffers
     uint32_t k6400;      // 0x64006400 in a vector register (identity DPP move: not a literal)
     u32x4 qhi[KS], qlo[KS];
     float4_t acc[NCB];
@@ -271,21 +287,50 @@ struct MqWave {
         for (int c = 0; c < NCB; c++) acc[c] = (float4_t){0.f, 0.f, 0.f, 0.f};
     }
 
-    // INT4 page pair of unit step s (s >= n8): pages p0 + 2 (s - n8) and the next (clamped).
-    __device__ void load4(Buf<false>& b, int s) const
+    // Page ids of INT4 step s (s >= n8): pages p0 + 2 (s - n8) and the next (clamped to the last).
+    __device__ __forceinline__ void step_pages(int s, uint32_t& pa, uint32_t& pb) const
     {
-        const int pi = p0 + 2 * (s - a.n8);
-        const uint32_t pa = (uint32_t)mq_uniform(btrow + pi);
-        const uint32_t pb = (uint32_t)mq_uniform(btrow + (pi + 1 < p1 ? pi + 1 : pi));
-        // the lane picks its page id first: one 32x32 -> 64-bit multiply-add per pointer
+        // wave-uniform by construction; readfirstlane lets the compiler see it, so that the block
+        // table is read with scalar loads (a vector load here would make the loop wait on vmcnt)
+        const int pi = __builtin_amdgcn_readfirstlane(p0 + 2 * (s - a.n8));
+        const int pj = __builtin_amdgcn_readfirstlane(pi + 1 < p1 ? pi + 1 : pi);
+        pa = (uint32_t)mq_uniform(btrow + pi);
+        pb = (uint32_t)mq_uniform(btrow + pj);
+    }
+
+    // Copies the two page blocks of a step into stage buffer st: CPB instructions per block, each
+    // moving 16 bytes per lane with every lane active, so that a step is always 2 * CPB
+    // instructions.  In the last one, the lanes past the block's end re-read its last 128 bytes
+    // into the padding of the staged block (read inside the block, never used).
+    __device__ __forceinline__ void stage_copy(uint32_t pa, uint32_t pb, int st) const
+    {
+        __attribute__((address_space(3))) uint8_t* dst = ring + st * STAGE;
+#pragma unroll
+        for (int x = 0; x < 2; x++) {
+            const uint8_t* src = hbase + (uint64_t)(x ? pb : pa) * pstride;
+#pragma unroll
+            for (int i = 0; i < CPB; i++) {
+                int off = 1024 * i + 16 * lane;
+                if (1024 * (i + 1) > IB) off = off < IB ? off : IB - 128 + 16 * (lane & 7);
+                __builtin_amdgcn_global_load_lds((const void*)(src + off),
+                                                 (__attribute__((address_space(3))) void*)(dst + x * SB + 1024 * i), 16,
+                                                 0, 0);
+            }
+        }
+    }
+
+    // The operands of an INT4 step from stage buffer st (page A block, then page B block).
+    __device__ __forceinline__ void stage_read(Buf<false>& b, int st) const
+    {
+        const __attribute__((address_space(3))) uint8_t* base = ring + st * STAGE;
         const int kslot = 8 * ((n >> 2) & 1) + (n & 3);
-        const uint8_t* kp = hbase + (uint64_t)(n < 8 ? pa : pb) * pstride + kslot * 16;
-        const uint8_t* vp = hbase + (uint64_t)(g < 2 ? pa : pb) * pstride;
+        const __attribute__((address_space(3))) uint8_t* kp = base + (n < 8 ? 0 : SB) + kslot * 16;
+        const __attribute__((address_space(3))) uint8_t* vp = base + (g < 2 ? 0 : SB);
         if constexpr (D == 128) {
             kp += 256 * g;
 #pragma unroll
             for (int t = 0; t < 2; t++) {
-                const u32x4 w = ld16(kp + 64 * t);
+                const u32x4 w = *(const __attribute__((address_space(3))) u32x4*)(kp + 64 * t);
 #pragma unroll
                 for (int j = 0; j < 4; j++) b.k[t][j] = w[j];
             }
@@ -293,16 +338,17 @@ struct MqWave {
             kp += 256 * (g >> 1) + 8 * (g & 1);
 #pragma unroll
             for (int t = 0; t < 2; t++) {
-                const u32x2 w = ld8(kp + 64 * t);
+                const u32x2 w = *(const __attribute__((address_space(3))) u32x2*)(kp + 64 * t);
                 b.k[t][0] = w[0];
                 b.k[t][1] = w[1];
             }
         }
 #pragma unroll
-        for (int c = 0; c < NCB; c++) b.v[c][0] = ld4(vp + 8 * D + (16 * c + n) * 8 + 4 * (g & 1));
+        for (int c = 0; c < NCB; c++)
+            b.v[c][0] = *(const __attribute__((address_space(3))) uint32_t*)(vp + 8 * D + (16 * c + n) * 8 + 4 * (g & 1));
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-            const u32x4 w = ld16(vp + 16 * D + 64 * (g & 1) + 16 * j);
+            const u32x4 w = *(const __attribute__((address_space(3))) u32x4*)(vp + 16 * D + 64 * (g & 1) + 16 * j);
 #pragma unroll
             for (int i = 0; i < 4; i++) b.sc[4 * j + i] = w[i];
         }
@@ -476,6 +522,7 @@ struct MqWave {
     }
 
     // INT8 steps [s0, s1): a few per task (the protection slots), one buffer.
+    // (one buffer: a second one would not fit the register budget of 2 waves per SIMD)
     __device__ void run8(int s0, int s1)
     {
         for (int s = s0; s < s1; s++) {
@@ -501,20 +548,34 @@ struct MqWave {
             compute<false, false>(b, s);
     }
 
-    // INT4 steps [s0, s1) with the next step's loads in flight during each step; a load past the
-    // end repeats the last step's addresses and is not used.
+    // INT4 steps [s0, s1) through the LDS ring: the copies of the next kMqStages - 1 steps are in
+    // flight while a step is computed.  Every iteration issues exactly one step's copies (past the
+    // end they repeat the last step and are never read), so the wait for the oldest one is a fixed
+    // count.  A stage is refilled only in the iteration after its operands were read (and used).
     __device__ void run4(int s0, int s1)
     {
         if (s0 >= s1) return;
-        Buf<false> b0, b1;
-        load4(b0, s0);
-        for (int s = s0; s < s1; s += 2) {
-            load4(b1, s + 1 < s1 ? s + 1 : s);
-            step4(b0, s);
-            if (s + 1 >= s1) break;
-            load4(b0, s + 2 < s1 ? s + 2 : s + 1);
-            step4(b1, s + 1);
+        constexpr int PER = 2 * CPB; // copy instructions per step
+        uint32_t pa, pb;
+#pragma unroll
+        for (int j = 0; j < kMqStages - 1; j++) {
+            step_pages(min(s0 + j, s1 - 1), pa, pb);
+            stage_copy(pa, pb, j);
         }
+        step_pages(min(s0 + kMqStages - 1, s1 - 1), pa, pb);
+        int st = 0;
+        for (int s = s0; s < s1; s++) {
+            __builtin_amdgcn_sched_barrier(0);
+            stage_copy(pa, pb, st == 0 ? kMqStages - 1 : st - 1);
+            step_pages(min(s + kMqStages, s1 - 1), pa, pb);
+            wait_vmcnt<(kMqStages - 1) * PER>();
+            __builtin_amdgcn_sched_barrier(0);
+            Buf<false> b;
+            stage_read(b, st);
+            step4(b, s);
+            st = st + 1 == kMqStages ? 0 : st + 1;
+        }
+        wait_vmcnt<0>();
     }
 
     __device__ void finish(int task)
@@ -545,6 +606,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     const int wave = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
     if (wave >= a.tasks) return;
     const int lane = (int)(threadIdx.x & 63);
+    __shared__ __align__(16) uint8_t mq_ring[4][kMqStages * 2 * 1024 * ((16 * D + 128 + 1023) / 1024)];
     const int lo = mq_find_entry<false>(a, wave, lane);
     MqEntry e;
     e.seq = mq_uniform(&a.entries[lo].seq);
@@ -562,6 +624,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     const int rt = local - chunk * nrt;
 
     MqWave<D, G, FMT> W(a, lane);
+    W.ring = (__attribute__((address_space(3))) uint8_t*)mq_ring[__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)];
     W.seq = e.seq;
     W.L = e.len;
     W.head = head;
@@ -581,10 +644,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
         W.p1 = (e.len + kPageSize - 1) / kPageSize;
         W.t8 = nullptr;
     }
-    W.prologue(e, rt);
     const int s0 = chunk * a.spc;
     const int s1 = s0 + a.spc < e.steps ? s0 + a.spc : e.steps;
     const int n8 = FMT == FMT_INT8 ? e.steps : a.n8;
+    W.prologue(e, rt);
     W.run8(s0, s1 < n8 ? s1 : n8);
     if (FMT == FMT_INT4_PROT) W.run4(s0 > n8 ? s0 : n8, s1);
     W.finish(wave);
