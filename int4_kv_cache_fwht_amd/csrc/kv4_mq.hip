@@ -137,13 +137,15 @@ __device__ __forceinline__ void split_hilo(const float (&x)[8], u32x4& hi, u32x4
 }
 
 // hi + lo fp16 of eight floats (same element order), hi truncated toward zero: the residual
-// x - hi is exact in fp32 and its own fp16 truncation leaves about 2^-20 of x.
-__device__ __forceinline__ void split_hilo_rtz(const float (&x)[8], u32x4& hi, u32x4& lo)
+// x - hi is exact in fp32 and its own fp16 truncation leaves about 2^-20 of x.  m1 is -1 held in a
+// vector register, so that each residual stays one v_fma_mix_f32 reading hi's fp16 half (with a
+// literal -1 the compiler turns the fma into a conversion and a subtraction).
+__device__ __forceinline__ void split_hilo_rtz(const float (&x)[8], u32x4& hi, u32x4& lo, float m1)
 {
 #pragma unroll
     for (int s = 0; s < 4; s++) {
         const half2_t h = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(x[s], x[s + 4]));
-        const float r0 = fmaf((float)h[0], -1.f, x[s]), r1 = fmaf((float)h[1], -1.f, x[s + 4]);
+        const float r0 = fmaf((float)h[0], m1, x[s]), r1 = fmaf((float)h[1], m1, x[s + 4]);
         hi[s] = __builtin_bit_cast(uint32_t, h);
         lo[s] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(r0, r1));
     }
@@ -211,12 +213,14 @@ struct MqWave {
     float m_ref = -__builtin_inff(), lsum = 0.f, zsum = 0.f, Ar = 0.f, Br = 0.f;
     __attribute__((address_space(3))) uint8_t* ring; // this wave's kMqStages INT4 stage buffers
     uint32_t k6400;      // 0x64006400 in a vector register (identity DPP move: not a literal)
+    float m1;            // -1 in a vector register (the same)
     u32x4 qhi[KS], qlo[KS];
     float4_t acc[NCB];
 
     __device__ MqWave(const MqArgs& args, int l)
         : a(args), lane(l), n(l & 15), g(l >> 4),
-          k6400((uint32_t)__builtin_amdgcn_update_dpp(0, 0x64006400, 0xE4, 0xF, 0xF, false))
+          k6400((uint32_t)__builtin_amdgcn_update_dpp(0, 0x64006400, 0xE4, 0xF, 0xF, false)),
+          m1(as_float((uint32_t)__builtin_amdgcn_update_dpp(0, (int)0xBF800000u, 0xE4, 0xF, 0xF, false)))
     {
     }
 
@@ -478,7 +482,15 @@ struct MqWave {
             st[t] = fmaf(lo_half(d0), r * Ar, fmaf(hi_half(d0), Br, 0.f));
             ok[t] = FULL || pos[t] <= pos_r;
             smax = ok[t] ? fmaxf(smax, st[t]) : smax;
-            svmax = ok[t] ? max(svmax, d1 & 0xFFFFu) : svmax;
+            if (!FULL) svmax = ok[t] ? max(svmax, d1 & 0xFFFFu) : svmax;
+        }
+        if (FULL) {
+            // every slot read: the largest s_V pattern by 16-bit maxima of the low halves
+            typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+            u16x2 mv = __builtin_bit_cast(u16x2, b.sc[1]);
+#pragma unroll
+            for (int t = 1; t < 8; t++) mv = __builtin_elementwise_max(mv, __builtin_bit_cast(u16x2, b.sc[2 * t + 1]));
+            svmax = mv.x;
         }
         float wmax = smax + (float)(svmax >> 10);
         wmax = fmaxf(wmax, lane_xor16(wmax));
@@ -511,7 +523,7 @@ struct MqWave {
             P[t] = ok[t] ? fmaf(lo_half(d1), p, 0.f) : 0.f;
         }
         u32x4 phi, plo;
-        split_hilo_rtz(P, phi, plo);
+        split_hilo_rtz(P, phi, plo, m1);
 #pragma unroll
         for (int c = 0; c < NCB; c++) {
             const u32x4 bv = IS8 ? centre<MID>(spread_int8(b.v[c][0], b.v[c][1]))
