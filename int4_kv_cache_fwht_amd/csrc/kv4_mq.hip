@@ -612,10 +612,23 @@ struct MqWave {
     }
 };
 
+// Workgroup order for the XCDs.  Tasks run with the row tile fastest, so the 16 row tiles of a
+// (sequence, kv head, chunk) -- four consecutive workgroups -- read the same pages.  Workgroups are
+// dispatched to the 8 XCDs of the chip in turn (b on XCD b % 8), each with its own L2; this
+// bijection of [0, 32 floor(n / 32)) gives each group of four consecutive task blocks one XCD, so
+// that their re-reads of the pages hit the same L2.  The last n % 32 blocks keep their order.
+__device__ __forceinline__ int xcd_grouped_block(int b, int nb)
+{
+    const int full = nb / 32 * 32;
+    if (b >= full) return b;
+    const int xcd = b & 7, slot = b >> 3;
+    return (slot >> 2) * 32 + xcd * 4 + (slot & 3);
+}
+
 template <int D, int G, int FMT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void mq_split_kernel(MqArgs a)
 {
-    const int wave = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+    const int wave = xcd_grouped_block((int)blockIdx.x, (int)gridDim.x) * 4 + (int)(threadIdx.x >> 6);
     if (wave >= a.tasks) return;
     const int lane = (int)(threadIdx.x & 63);
     __shared__ __align__(16) uint8_t mq_ring[4][kMqStages * 2 * 1024 * ((16 * D + 128 + 1023) / 1024)];
