@@ -48,7 +48,10 @@ __device__ __forceinline__ void static_for(F&& f)
     }
 }
 
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ float as_float(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ u16x2 as_u16x2(uint32_t u) { return __builtin_bit_cast(u16x2, u); }
 __device__ __forceinline__ uint32_t as_uint(float f) { return __builtin_bit_cast(uint32_t, f); }
 
 __device__ __forceinline__ float f16_bits_to_float(uint32_t bits16)

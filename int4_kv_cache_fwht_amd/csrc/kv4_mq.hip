@@ -486,10 +486,9 @@ struct MqWave {
         }
         if (FULL) {
             // every slot read: the largest s_V pattern by 16-bit maxima of the low halves
-            typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-            u16x2 mv = __builtin_bit_cast(u16x2, b.sc[1]);
+            u16x2 mv = as_u16x2(b.sc[1]);
 #pragma unroll
-            for (int t = 1; t < 8; t++) mv = __builtin_elementwise_max(mv, __builtin_bit_cast(u16x2, b.sc[2 * t + 1]));
+            for (int t = 1; t < 8; t++) mv = __builtin_elementwise_max(mv, as_u16x2(b.sc[2 * t + 1]));
             svmax = mv.x;
         }
         float wmax = smax + (float)(svmax >> 10);
