@@ -1036,14 +1036,41 @@ __global__ __launch_bounds__(64 * G) void merge_kernel(DecodeArgs a)
     const float* ml = a.part_ml + ((w0 + u) * G + i) * 2;
     const float* po = a.part_o + ((w0 + u) * G + i) * D + lane;
     float M = -INFINITY;
-    for (int j0 = 0; j0 < n; j0 += 64) {
-        const int j = j0 + lane;
-        M = fmaxf(M, j < n ? ml[(int64_t)j * G * 2] : -INFINITY);
-    }
-    M = wave_max_u(M);
     float Ls = 0.f, O[NHV];
 #pragma unroll
     for (int hv = 0; hv < NHV; hv++) O[hv] = 0.f;
+    if (n >= 1 && n <= 16) {
+        // the usual case: every (m, l) and every output row are loaded before any is used (one
+        // memory round trip; rows past n repeat the last partial and get weight 0).  Same sums in
+        // the same order as the general loop below.
+        const float mj = lane < n ? ml[(int64_t)lane * G * 2] : -INFINITY;
+        const float lj = lane < n ? ml[(int64_t)lane * G * 2 + 1] : 0.f;
+        float pv[16][NHV];
+#pragma unroll
+        for (int k = 0; k < 16; k++)
+#pragma unroll
+            for (int hv = 0; hv < NHV; hv++) pv[k][hv] = po[(int64_t)(k < n ? k : n - 1) * G * D + 64 * hv];
+        M = wave_max_u(mj);
+        if (M != -INFINITY) {
+            const float fj = (mj == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mj - M);
+            Ls = wave_sum_u(fj * lj);
+#pragma unroll
+            for (int k = 0; k < 16; k++) {
+                if (k < n) {
+                    const float f = as_float((uint32_t)__builtin_amdgcn_readlane((int)as_uint(fj), k));
+#pragma unroll
+                    for (int hv = 0; hv < NHV; hv++) O[hv] = fmaf(pv[k][hv], f, O[hv]);
+                }
+            }
+        }
+        M = -INFINITY; // the general loop below is skipped
+    } else {
+        for (int j0 = 0; j0 < n; j0 += 64) {
+            const int j = j0 + lane;
+            M = fmaxf(M, j < n ? ml[(int64_t)j * G * 2] : -INFINITY);
+        }
+        M = wave_max_u(M);
+    }
     if (M != -INFINITY) {
         for (int j0 = 0; j0 < n; j0 += 64) {
             const int j = j0 + lane;
