@@ -764,6 +764,18 @@ struct DecodeWave {
         k1 = (int)((s_end < ue ? s_end : ue) - wb);
     }
 
+    // The waves holding a unit's first and last work step (global steps step_begin +
+    // kUnitStartSteps and ue - 1, inside this wave's slice [s, s_end) from s on) record
+    // themselves: the merge reads the unit's partials w0 + u .. w1 + u.
+    __device__ __forceinline__ void mark_unit(const DecodeUnit& U, int64_t ue, int64_t s, int u) const
+    {
+        const int64_t wb = U.step_begin + kUnitStartSteps;
+        if (lane == 0) {
+            if (wb >= s && wb < s_end) a.unit_waves[2 * u] = (int32_t)w;
+            if (ue - 1 >= s && ue - 1 < s_end) a.unit_waves[2 * u + 1] = (int32_t)w;
+        }
+    }
+
     // ---- the wave's steps [s, s_end), starting in unit u (quantized formats) ----
     __device__ void run(int u, int64_t s)
     {
@@ -773,6 +785,7 @@ struct DecodeWave {
             unit_at(u, U, ue);
             int k0, k1;
             unit_slice(U, ue, s, k0, k1);
+            mark_unit(U, ue, s, u);
             if (k1 > k0) {
                 run_unit(U, k0, k1);
                 epilogue(w + u);
@@ -913,6 +926,7 @@ struct DecodeWave {
             unit_at(u, U, ue);
             int k0, k1;
             unit_slice(U, ue, s, k0, k1);
+            mark_unit(U, ue, s, u);
             if (k1 > k0) {
                 prologue_bf16(U);
                 for (int k = k0; k < k1; k++) bf16_step(U, k);
@@ -994,19 +1008,6 @@ void decode_split_kernel(DecodeArgs a)
 // (H is symmetric: the same FWHT and the fl32(1/sqrt(b)) scale) in registers
 // ---------------------------------------------------------------------------------------------
 
-__device__ __forceinline__ int64_t wave_of_step(int64_t step, int64_t T, int64_t W)
-{
-    const int64_t w = ((step + 1) * W - 1) / T;
-    return w < W - 1 ? w : W - 1;
-}
-
-// The wave whose slice holds global step `step` (the inverse of wave_slice).
-__device__ __forceinline__ int64_t wave_of_step(const DecodeArgs& a, int64_t step)
-{
-    if (step < a.steps1) return wave_of_step(step, a.steps1, a.n_waves1);
-    return a.n_waves1 + wave_of_step(step - a.steps1, a.total_steps - a.steps1, a.n_waves - a.n_waves1);
-}
-
 // OUT16: the output rows are bf16 (round to nearest even of the fp32 result) at a.out.
 template <int D, int G, int FMT, bool OUT16 = false>
 __global__ __launch_bounds__(64 * G) void merge_kernel(DecodeArgs a)
@@ -1017,19 +1018,18 @@ __global__ __launch_bounds__(64 * G) void merge_kernel(DecodeArgs a)
     const int i = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     DecodeUnit U;
-    int64_t se;
     if (a.n_arg > 0) {
         const int n8 = (FMT == FMT_INT4_PROT && a.sinks + a.recent > 0)
                            ? (a.sinks + a.recent + kInt8StepSlots - 1) / kInt8StepSlots
                            : 0;
-        arg_unit_scalar<FMT>(a, n8, u, U, se);
+        int64_t ue;
+        arg_unit_scalar<FMT>(a, n8, u, U, ue);
     } else {
         U = ld_unit(a.units, u);
-        se = (u + 1 < a.n_units) ? ld_uniform(&a.units[u + 1].step_begin) : a.total_steps;
     }
-    // the waves whose slices hold work steps of the unit (after its start charge)
-    const int64_t sb = U.step_begin + kUnitStartSteps;
-    const int64_t w0 = wave_of_step(a, sb), w1 = wave_of_step(a, se - 1);
+    // the first and last wave holding work steps of the unit (after its start charge), as the
+    // split kernel recorded them
+    const int64_t w0 = ld_uniform(a.unit_waves + 2 * u), w1 = ld_uniform(a.unit_waves + 2 * u + 1);
     const int n = (int)(w1 - w0 + 1);
     // partial j of this unit sits at index w0 + u + j.  Lane j of a round of 64 holds partial
     // j's (m, l): one vector load per round instead of a scalar load (and its wait) per partial.

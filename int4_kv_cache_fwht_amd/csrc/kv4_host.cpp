@@ -246,6 +246,7 @@ struct DeviceGuard {
 // call 356 + 9 against 359 + 8 us, and the 64-sequence Qwen3-8B layer 71 against 76 us.
 int64_t auto_waves(const kv4_cache* h, int64_t /*total_steps*/) { return h->resident_waves; }
 
+
 int64_t max_waves(const kv4_cache* h)
 {
     int64_t w = 2 * (int64_t)h->resident_waves;
@@ -259,7 +260,7 @@ size_t decode_ws_bytes(const kv4_cache* h, int64_t n_units, int64_t waves)
     const int D = h->st.cfg.d;
     const int64_t parts = waves + n_units;
     return align_up((size_t)n_units * sizeof(kv4::DecodeUnit)) + align_up((size_t)parts * G * 2 * sizeof(float)) +
-           align_up((size_t)parts * G * D * sizeof(float));
+           align_up((size_t)parts * G * D * sizeof(float)) + align_up((size_t)n_units * 2 * sizeof(int32_t));
 }
 
 // Multi-query split tasks, in rounds of resident waves by the most row tiles (of kMqRows query rows)
@@ -643,6 +644,7 @@ kv4_status decode_impl(kv4_cache_t h, int32_t n_seqs, const int32_t* seq_ids, co
     a.units = (const kv4::DecodeUnit*)ws;
     a.part_ml = (float*)(ws + align_up(ubytes));
     a.part_o = (float*)(ws + align_up(ubytes) + align_up((size_t)parts * G * 2 * sizeof(float)));
+    a.unit_waves = (int32_t*)((uint8_t*)a.part_o + align_up((size_t)parts * G * D * sizeof(float)));
     a.out = out;
     a.total_steps = total;
     a.steps1 = T1;

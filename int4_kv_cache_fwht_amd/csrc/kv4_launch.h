@@ -50,6 +50,7 @@ struct DecodeArgs {
     const DecodeUnit* units;  // device copy of the plan
     float* part_ml;           // [(W + n_units)][G][2] : (reference max in log2 units, sum)
     float* part_o;            // [(W + n_units)][G][D]
+    int32_t* unit_waves;      // [n_units][2]: first and last wave holding work steps of the unit
     float* out;               // fp32 [entries][hq][D]
     int64_t total_steps;
     // two rounds of waves: waves [0, n_waves1) share the first steps1 global steps, waves
