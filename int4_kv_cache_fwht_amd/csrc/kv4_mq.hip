@@ -677,15 +677,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     W.finish(wave);
 }
 
-template <int D, int G, bool ROT>
+// Merge waves: one per (row tile, RQ of its rows); lane l holds output dims DPM l .. DPM l + DPM - 1.
+// With RQ > 1 the rows share the wave's entry lookup and their loads are issued together, which
+// pays once one row per wave would take several rounds of resident waves (many row tiles); with
+// few tiles one row per wave keeps more rows in flight.  Row r's chunk partials are merged in chunk
+// order (log-sum-exp against their maximum), then the inverse FWHT is applied and the row stored.
+constexpr int kMqMergeWideWaves = 16384; // one-row waves from which RQ = 4 is used
+
+template <int D, int G, bool ROT, int RQ>
 __global__ __launch_bounds__(256) void mq_merge_kernel(MqArgs a)
 {
     constexpr int DPM = D / 64;
     constexpr int QT = kMqRows / G;
+    constexpr int NC = 8; // chunk count of the one-round-trip path
     const int wave = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
-    if (wave >= a.groups * kMqRows) return;
+    if (wave >= a.groups * (kMqRows / RQ)) return;
     const int lane = (int)(threadIdx.x & 63);
-    const int grp = wave / kMqRows, r = wave % kMqRows;
+    const int grp = wave / (kMqRows / RQ), r0 = (wave % (kMqRows / RQ)) * RQ;
     const int lo = mq_find_entry<true>(a, grp, lane);
     const int nq = mq_uniform(&a.entries[lo].nq);
     const int qrow0 = mq_uniform(&a.entries[lo].qrow0);
@@ -695,75 +703,122 @@ __global__ __launch_bounds__(256) void mq_merge_kernel(MqArgs a)
     const int nrt = (nq * G + kMqRows - 1) / kMqRows;
     const int local = grp - grp0;
     const int head = local / nrt, rt = local - head * nrt;
-    const int jq = rt * QT + r / G, gi = r % G;
-    if (jq >= nq) return;
-    // chunk c's partial of this row sits in task slot T(c); lane c of a round of 64 holds its
-    // (m, l), one vector load per round
-    const int64_t T0 = (int64_t)task0 + (int64_t)head * nch * nrt + rt; // T(c) = T0 + c nrt
-    float M = -__builtin_inff();
-    for (int c0 = 0; c0 < nch; c0 += 64) {
-        const int c = c0 + lane;
-        M = fmaxf(M, c < nch ? a.part_ml[((T0 + (int64_t)c * nrt) * kMqRows + r) * 2] : -__builtin_inff());
+    if (rt * QT + r0 / G >= nq) return; // every row of the wave lies past the entry's queries
+    // chunk c's partials of the tile sit in task slot T(c) = T0 + c nrt: (m, l) of row r at
+    // part_ml[(T(c) kMqRows + r) 2], its output at part_o[(T(c) kMqRows + r) D]
+    const int64_t T0 = (int64_t)task0 + (int64_t)head * nch * nrt + rt;
+    const int64_t cstride = (int64_t)nrt * kMqRows; // rows from one chunk's slot to the next
+    float l[RQ], o[RQ][DPM];
+#pragma unroll
+    for (int q = 0; q < RQ; q++) {
+        l[q] = 0.f;
+#pragma unroll
+        for (int k = 0; k < DPM; k++) o[q][k] = 0.f;
     }
-    M = wave_max_u(M);
-    float l = 0.f, o[DPM];
+    if (nch <= NC) {
+        // every (m, l) and every output row of the RQ rows loaded before the first is used; lane c
+        // holds chunk c's (m, l), chunks past nch repeat the last one's outputs and get weight 0
+        float mj[RQ], lj[RQ], pv[NC][RQ][DPM];
 #pragma unroll
-    for (int k = 0; k < DPM; k++) o[k] = 0.f;
-    for (int c0 = 0; c0 < nch; c0 += 64) {
-        const int c = c0 + lane;
-        const float* mlc = a.part_ml + ((T0 + (int64_t)c * nrt) * kMqRows + r) * 2;
-        const float m = c < nch ? mlc[0] : -__builtin_inff();
-        const float lc = c < nch ? mlc[1] : 0.f;
-        const float wgt = exp2f(m - M);
-        l += wave_sum_u(wgt * lc);
-        // the outputs in chunk order, each weight read from its lane; the loads of 8 chunks are
-        // issued before the first of them is used (8 keeps 8 waves per SIMD)
-        const int cn = __builtin_amdgcn_readfirstlane(nch - c0 < 64 ? nch - c0 : 64);
-        // chunk c's outputs: a wave-uniform base plus the lane's offset
-        const float* obase = a.part_o + (T0 * kMqRows + r) * D;
-        const int64_t ostride = (int64_t)nrt * kMqRows * D;
-        for (int cb = 0; cb < cn; cb += 8) {
-            float pv[8][DPM];
+        for (int q = 0; q < RQ; q++) {
+            const float* mlc = a.part_ml + ((T0 * kMqRows + r0 + q) + (int64_t)lane * cstride) * 2;
+            mj[q] = lane < nch ? mlc[0] : -__builtin_inff();
+            lj[q] = lane < nch ? mlc[1] : 0.f;
+        }
 #pragma unroll
-            for (int k = 0; k < 8; k++) {
-                const float* po = obase + (int64_t)(c0 + cb + k) * ostride;
+        for (int c = 0; c < NC; c++) {
+            const float* po = a.part_o + ((T0 * kMqRows + r0) + (int64_t)(c < nch ? c : nch - 1) * cstride) * D + lane * DPM;
 #pragma unroll
-                for (int q = 0; q < DPM; q++) pv[k][q] = cb + k < cn ? po[lane * DPM + q] : 0.f;
+            for (int q = 0; q < RQ; q++)
+#pragma unroll
+                for (int k = 0; k < DPM; k++) pv[c][q][k] = po[q * D + k];
+        }
+#pragma unroll
+        for (int q = 0; q < RQ; q++) {
+            const float M = wave_max_u(mj[q]);
+            const float wgt = exp2f(mj[q] - M);
+            l[q] = wave_sum_u(wgt * lj[q]);
+#pragma unroll
+            for (int c = 0; c < NC; c++) {
+                if (c < nch) {
+                    const float w = as_float((uint32_t)__builtin_amdgcn_readlane((int)as_uint(wgt), c));
+#pragma unroll
+                    for (int k = 0; k < DPM; k++) o[q][k] = fmaf(w, pv[c][q][k], o[q][k]);
+                }
             }
+        }
+    } else {
 #pragma unroll
-            for (int k = 0; k < 8; k++) {
-                if (cb + k < cn) {
-                    const float w = as_float((uint32_t)__builtin_amdgcn_readlane((int)as_uint(wgt), cb + k));
+        for (int q = 0; q < RQ; q++) {
+            const int r = r0 + q;
+            float M = -__builtin_inff();
+            for (int c0 = 0; c0 < nch; c0 += 64) {
+                const int c = c0 + lane;
+                M = fmaxf(M, c < nch ? a.part_ml[((T0 * kMqRows + r) + (int64_t)c * cstride) * 2] : -__builtin_inff());
+            }
+            M = wave_max_u(M);
+            for (int c0 = 0; c0 < nch; c0 += 64) {
+                const int c = c0 + lane;
+                const float* mlc = a.part_ml + ((T0 * kMqRows + r) + (int64_t)c * cstride) * 2;
+                const float m = c < nch ? mlc[0] : -__builtin_inff();
+                const float lc = c < nch ? mlc[1] : 0.f;
+                const float wgt = exp2f(m - M);
+                l[q] += wave_sum_u(wgt * lc);
+                // the outputs in chunk order, each weight read from its lane; the loads of 8 chunks
+                // are issued before the first of them is used
+                const int cn = __builtin_amdgcn_readfirstlane(nch - c0 < 64 ? nch - c0 : 64);
+                const float* obase = a.part_o + (T0 * kMqRows + r) * D;
+                for (int cb = 0; cb < cn; cb += 8) {
+                    float pw[8][DPM];
 #pragma unroll
-                    for (int q = 0; q < DPM; q++) o[q] = fmaf(w, pv[k][q], o[q]);
+                    for (int k = 0; k < 8; k++) {
+                        const float* po = obase + (int64_t)(c0 + cb + k) * cstride * D;
+#pragma unroll
+                        for (int d = 0; d < DPM; d++) pw[k][d] = cb + k < cn ? po[lane * DPM + d] : 0.f;
+                    }
+#pragma unroll
+                    for (int k = 0; k < 8; k++) {
+                        if (cb + k < cn) {
+                            const float w = as_float((uint32_t)__builtin_amdgcn_readlane((int)as_uint(wgt), cb + k));
+#pragma unroll
+                            for (int d = 0; d < DPM; d++) o[q][d] = fmaf(w, pw[k][d], o[q][d]);
+                        }
+                    }
                 }
             }
         }
     }
-    const float inv = 1.f / l;
 #pragma unroll
-    for (int k = 0; k < DPM; k++) o[k] *= inv;
-    if (ROT) {
-        // o H_bd (Sylvester H is symmetric, so this is also o H_bd^T), stages h = 1, 2, ..., b/2
-        if (DPM == 2 && a.block > 1) {
-            const float u = o[0], w = o[DPM - 1];
-            o[0] = u + w;
-            o[DPM - 1] = u - w;
-        }
-        static_for<0, 6>([&](auto S) {
-            constexpr int M = 1 << S;
-            if (M * DPM < a.block) {
-                const float sgn = (lane & M) ? -1.f : 1.f;
+    for (int q = 0; q < RQ; q++) {
+        const int r = r0 + q;
+        const int jq = rt * QT + r / G, gi = r % G;
+        if (jq >= nq) continue; // (wave-uniform)
+        float x[DPM];
+        const float inv = 1.f / l[q];
 #pragma unroll
-                for (int k = 0; k < DPM; k++) o[k] = butterfly_xor<M>(o[k], sgn);
+        for (int k = 0; k < DPM; k++) x[k] = o[q][k] * inv;
+        if (ROT) {
+            // x H_bd (Sylvester H is symmetric, so this is also x H_bd^T), stages h = 1, 2, ..., b/2
+            if (DPM == 2 && a.block > 1) {
+                const float u = x[0], w = x[DPM - 1];
+                x[0] = u + w;
+                x[DPM - 1] = u - w;
             }
-        });
+            static_for<0, 6>([&](auto S) {
+                constexpr int M = 1 << S;
+                if (M * DPM < a.block) {
+                    const float sgn = (lane & M) ? -1.f : 1.f;
 #pragma unroll
-        for (int k = 0; k < DPM; k++) o[k] *= a.cb;
+                    for (int k = 0; k < DPM; k++) x[k] = butterfly_xor<M>(x[k], sgn);
+                }
+            });
+#pragma unroll
+            for (int k = 0; k < DPM; k++) x[k] *= a.cb;
+        }
+        float* out = a.out + ((int64_t)(qrow0 + jq) * a.hq + head * G + gi) * D + lane * DPM;
+#pragma unroll
+        for (int k = 0; k < DPM; k++) out[k] = x[k];
     }
-    float* out = a.out + ((int64_t)(qrow0 + jq) * a.hq + head * G + gi) * D + lane * DPM;
-#pragma unroll
-    for (int k = 0; k < DPM; k++) out[k] = o[k];
 }
 
 template <int D, int G, int FMT>
@@ -776,9 +831,12 @@ hipError_t split_dispatch(const MqArgs& a, hipStream_t stream, const KernelTimer
 template <int D, int G>
 hipError_t merge_dispatch(const MqArgs& a, hipStream_t stream, const KernelTimer& tm)
 {
-    const int64_t waves = (int64_t)a.groups * kMqRows;
-    const int blocks = (int)((waves + 3) / 4);
-    return launch_kernel(mq_merge_kernel<D, G, true>, dim3(blocks), dim3(256), stream, tm, a);
+    if ((int64_t)a.groups * kMqRows >= kMqMergeWideWaves) {
+        const int blocks = (int)(((int64_t)a.groups * (kMqRows / 4) + 3) / 4);
+        return launch_kernel(mq_merge_kernel<D, G, true, 4>, dim3(blocks), dim3(256), stream, tm, a);
+    }
+    const int blocks = (int)(((int64_t)a.groups * kMqRows + 3) / 4);
+    return launch_kernel(mq_merge_kernel<D, G, true, 1>, dim3(blocks), dim3(256), stream, tm, a);
 }
 
 template <int D, int G, int FMT>
