@@ -158,3 +158,20 @@ def test_mq_errors():
     # nothing above changed the state: the cache still decodes as before
     out, ref = p.multi([0, 1], [10, 20], _q(30, 8, 64, seed=4))
     assert np.abs(out - ref).max() <= TOL
+
+
+def test_mq_wide_merge_long_entry():
+    """Many row tiles, so that the merge takes 4 rows per wave, with one long sequence among short
+    ones: the chunk size is set for the whole call, so the long sequence's rows merge over more than
+    64 chunks (the merge's general path, in rounds of 64 chunks)."""
+    _print_case("mq_wide_merge")
+    hq, hkv, d = 32, 8, 128
+    lens = [300] * 299 + [60000]
+    nqs = [4] * 300
+    p = Pair(hq, hkv, d, num_pages=9600, max_seqs=300, max_pps=3800, S=4, R=128, b=128)
+    _fill(p, lens, hkv, d, seed=31)
+    q = _q(sum(nqs), hq, d, seed=33)
+    out, ref = p.multi(list(range(len(lens))), nqs, q)
+    err = np.abs(out - ref).max()
+    print("mq wide merge max-abs", err, flush=True)
+    assert err <= TOL
