@@ -715,31 +715,42 @@ struct DecodeWave {
     }
 
     // ---- one unit's steps [k0, k1) (quantized formats): INT8 and INT4 steps in one pipeline ----
+    // The wave walks its n steps from a rotation r that a multiplicative hash of the wave index
+    // picks (step i of the walk is k0 + (i + r) mod n): waves with equal slices of one long
+    // sequence would otherwise stream addresses a fixed stride apart in lock step, which some
+    // strides map onto few memory channels.  The online softmax takes the steps in any order.
     __device__ void run_unit(const DecodeUnit& U, int k0, int k1)
     {
         const int p1 = (FMT == FMT_INT4_PROT) ? int4_p1(U.len) : 0;
-        Ids id = step_ids(U, k0, p1);
+        const int n = k1 - k0;
+        const int r = (int)(((uint32_t)w * 2654435761u >> 8) % (uint32_t)n);
+        // walk index i (clamped to the last: the trailing prefetch re-reads cached lines) -> step
+        auto at = [&](int i) {
+            i = min(i, n - 1) + r;
+            return k0 + (i >= n ? i - n : i);
+        };
+        Ids id = step_ids(U, at(0), p1);
         // query rows of the unit (issued first: the prologue waits for them only): lane l holds
         // 8 bf16 of head l / (D/8), dims 8 (l % (D/8)) .. +7
         const uint16_t* pq = a.q + ((int64_t)U.entry * (a.hkv * G) + U.head * G) * D + 8 * min(lane, QLANES - 1);
         const u32x4 qraw = *(const u32x4*)pq;
         Buf A, B;
-        load_step(U, k0, id, A);
-        id = step_ids(U, min(k0 + 1, k1 - 1), p1);
+        load_step(U, at(0), id, A);
+        id = step_ids(U, at(1), p1);
         prologue_q(qraw);
-        int k = k0;
+        int i = 0;
         while (true) {
             half4_t Ahi, Alo;
-            load_step(U, min(k + 1, k1 - 1), id, B); // step k + 1 (or step k again at the end: cached lines)
-            compute_qk(U, k, p1, A, Ahi, Alo);
-            id = step_ids(U, min(k + 2, k1 - 1), p1);
-            compute_pv(k, A, Ahi, Alo);
-            if (++k >= k1) break;
-            load_step(U, min(k + 1, k1 - 1), id, A);
-            compute_qk(U, k, p1, B, Ahi, Alo);
-            id = step_ids(U, min(k + 2, k1 - 1), p1);
-            compute_pv(k, B, Ahi, Alo);
-            if (++k >= k1) break;
+            load_step(U, at(i + 1), id, B);
+            compute_qk(U, at(i), p1, A, Ahi, Alo);
+            id = step_ids(U, at(i + 2), p1);
+            compute_pv(at(i), A, Ahi, Alo);
+            if (++i >= n) break;
+            load_step(U, at(i + 1), id, A);
+            compute_qk(U, at(i), p1, B, Ahi, Alo);
+            id = step_ids(U, at(i + 2), p1);
+            compute_pv(at(i), B, Ahi, Alo);
+            if (++i >= n) break;
         }
     }
 
