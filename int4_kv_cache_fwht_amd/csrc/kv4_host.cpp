@@ -264,12 +264,12 @@ size_t decode_ws_bytes(const kv4_cache* h, int64_t n_units, int64_t waves)
 }
 
 // Multi-query split tasks, in rounds of resident waves by the most row tiles (of kMqRows query rows)
-// any (sequence, kv head) has: two rounds at one tile, three at two to four, two above.  Smaller
-// chunks balance the waves of the few-tile calls, but each adds a partial per row tile; with one
-// tile the merge's share decides, with many tiles per chunk they only add partials and re-reads.
-// Qwen3-8B layer on MI355X (split + merge): 4 rows per sequence (one tile) 114 us with two rounds
-// against 118 with three; 16 rows 318 against 345 with two; 64 rows 1196 us with two rounds
-// against 1393 us with three.  n_q is read only where it is positive; the call validates it.
+// any (sequence, kv head) has: one round at one tile, three at two to four, two above.  Smaller
+// chunks balance the waves of the few-tile calls, but each adds a partial per row tile.  With one
+// tile, one round of chunks (the planner keeps the count within it) balances the waves and keeps
+// the merge short: on the Qwen3-8B layer (MI355X) 4 rows per sequence take 86-94 + 6.6 us (split +
+// merge) in one round against 100-104 + 10.4 us in two.  With many tiles per chunk, extra rounds
+// only add partials and re-reads.  n_q is read only where it is positive; the call validates it.
 int64_t mq_target_tasks(const kv4_cache* h, int32_t n_seqs, const int32_t* n_q)
 {
     const int G = h->st.cfg.hq / h->st.cfg.hkv;
@@ -277,7 +277,7 @@ int64_t mq_target_tasks(const kv4_cache* h, int32_t n_seqs, const int32_t* n_q)
     if (n_q)
         for (int32_t i = 0; i < n_seqs; i++)
             if (n_q[i] > 0) tiles = std::max<int64_t>(tiles, ((int64_t)n_q[i] * G + kv4::kMqRows - 1) / kv4::kMqRows);
-    return (tiles >= 2 && tiles <= 4 ? 3 : 2) * (int64_t)h->mq_resident_waves;
+    return (tiles <= 1 ? 1 : tiles <= 4 ? 3 : 2) * (int64_t)h->mq_resident_waves;
 }
 
 size_t mq_ws_bytes(const kv4_cache* h, const kv4::MqPlan& p)

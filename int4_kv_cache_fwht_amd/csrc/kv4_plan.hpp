@@ -8,6 +8,7 @@
 // Cache Quantization" (Abstract: sinks and recent context, a bounded number of positions).
 #pragma once
 
+#include <algorithm>
 #include <cstddef>
 #include <cstdint>
 #include <deque>
@@ -337,28 +338,63 @@ struct State {
         if (target_tasks < 1) target_tasks = 1;
         int64_t spc = (work + target_tasks - 1) / target_tasks;
         if (spc < 1) spc = 1;
+        // Each (sequence, kv head, row tile) rounds its chunk count up, so the count can pass the
+        // target, and the tasks past a whole number of resident rounds then run nearly alone at
+        // the end.  The chunk grows until the count fits, or until it covers the longest unit
+        // (one task per row tile, the smallest count there is).
+        int64_t max_steps = 1;
+        for (int i = 0; i < n_seqs; i++) max_steps = std::max<int64_t>(max_steps, mq_unit_steps(cfg, len[(size_t)ids[i]]));
+        auto count = [&](int64_t c) {
+            int64_t t = 0;
+            for (int i = 0; i < n_seqs; i++) {
+                const int64_t nrt = ((int64_t)n_q[i] * G + kMqRows - 1) / kMqRows;
+                t += (int64_t)cfg.hkv * nrt * ((mq_unit_steps(cfg, len[(size_t)ids[i]]) + c - 1) / c);
+            }
+            return t;
+        };
+        if (spc < max_steps && count(spc) > target_tasks) {
+            // the count does not grow with the chunk: the smallest chunk that fits, by bisection
+            // (count(lo) > target >= count(hi) throughout)
+            int64_t lo = spc, hi = max_steps;
+            if (count(hi) <= target_tasks) {
+                while (hi - lo > 1) {
+                    const int64_t mid = lo + (hi - lo) / 2;
+                    if (count(mid) > target_tasks)
+                        lo = mid;
+                    else
+                        hi = mid;
+                }
+            }
+            spc = hi;
+        }
         plan->entries.clear();
-        int64_t tasks = 0, groups = 0, qrow = 0;
+        int64_t qrow = 0;
         for (int i = 0; i < n_seqs; i++) {
             const int L = len[(size_t)ids[i]];
-            const int steps = mq_unit_steps(cfg, L);
-            const int64_t nrt = ((int64_t)n_q[i] * G + kMqRows - 1) / kMqRows;
-            const int64_t nch = (steps + spc - 1) / spc;
             MqEntry e;
             e.seq = ids[i];
             e.len = L;
             e.nq = n_q[i];
-            e.qrow0 = (int32_t)qrow;
+            e.qrow0 = (int32_t)qrow; // rows of the caller's q and out, in call order
+            e.steps = mq_unit_steps(cfg, L);
+            e.nch = (int32_t)((e.steps + spc - 1) / spc);
+            plan->entries.push_back(e);
+            qrow += n_q[i];
+            if (qrow >= ((int64_t)1 << 30)) return bad(UNSUPPORTED, "multi-query call too large");
+        }
+        // Tasks are numbered longest entry first.  Workgroups start in task order, so the longest
+        // tasks start first and the short ones fill in at the end.  (The kernels find an entry by
+        // its first task or merge group, which still increase along the list.)
+        std::stable_sort(plan->entries.begin(), plan->entries.end(),
+                         [](const MqEntry& x, const MqEntry& y) { return x.steps > y.steps; });
+        int64_t tasks = 0, groups = 0;
+        for (MqEntry& e : plan->entries) {
+            const int64_t nrt = ((int64_t)e.nq * G + kMqRows - 1) / kMqRows;
             e.task0 = (int32_t)tasks;
             e.grp0 = (int32_t)groups;
-            e.steps = steps;
-            e.nch = (int32_t)nch;
-            plan->entries.push_back(e);
-            tasks += (int64_t)cfg.hkv * nch * nrt;
+            tasks += (int64_t)cfg.hkv * e.nch * nrt;
             groups += (int64_t)cfg.hkv * nrt;
-            qrow += n_q[i];
-            if (tasks >= ((int64_t)1 << 27) || qrow >= ((int64_t)1 << 30))
-                return bad(UNSUPPORTED, "multi-query call too large");
+            if (tasks >= ((int64_t)1 << 27)) return bad(UNSUPPORTED, "multi-query call too large");
         }
         plan->tasks = tasks;
         plan->groups = groups;

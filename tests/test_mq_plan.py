@@ -91,9 +91,35 @@ def _emulate(st, entries, hq, hkv, S, R, fmt):
                         continue
                     pos_r = L - nq + jq
                     if pos <= pos_r:
-                        key = (ei, head, jq, r % G)
+                        key = (seq, head, jq, r % G)
                         seen.setdefault(key, []).append((pos, kind))
     return seen
+
+
+def _check_plan_order(st, entries, calls, hkv, G, target):
+    """Entries longest first; row offsets in call order; first tasks and merge groups contiguous
+    along the list; the task count within the target whenever one task per row tile allows it."""
+    nq_of = dict(calls)
+    rows_before, acc = {}, 0
+    for seq, nq in calls:
+        rows_before[seq] = acc
+        acc += nq
+    steps = [e[6] for e in entries]
+    assert steps == sorted(steps, reverse=True)
+    assert sorted(e[0] for e in entries) == sorted(nq_of)
+    t = g = 0
+    for seq, L, nq, qrow0, task0, grp0, st_, nch in entries:
+        assert nq == nq_of[seq] and qrow0 == rows_before[seq]
+        assert (task0, grp0) == (t, g)
+        nrt = -(-nq * G // 16)
+        t += hkv * nch * nrt
+        g += hkv * nrt
+        assert nch == -(-st_ // st["spc"])
+    assert (t, g) == (st["tasks"], st["groups"])
+    if st["groups"] <= target:
+        assert st["tasks"] <= target
+    else:
+        assert st["tasks"] == st["groups"]  # one chunk per (sequence, kv head, row tile)
 
 
 @pytest.mark.parametrize("hq,hkv,S,R,fmt,lens,nqs,target", [
@@ -117,14 +143,15 @@ def test_rows_attend_each_position_once_from_the_right_copy(driver, hq, hkv, S, 
         assert st["status"] == 0
         G = hq // hkv
         assert st["groups"] == sum(hkv * -(-nq * G // 16) for nq in nqs)
+        _check_plan_order(st, entries, list(enumerate(nqs)), hkv, G, target)
         seen = _emulate(st, entries, hq, hkv, S, R, fmt)
-        for ei, (L, nq) in enumerate(zip(lens, nqs)):
+        for seq, (L, nq) in enumerate(zip(lens, nqs)):
             for h in range(hkv):
                 for jq in range(nq):
                     for gi in range(G):
-                        got = sorted(seen.get((ei, h, jq, gi), []))
+                        got = sorted(seen.get((seq, h, jq, gi), []))
                         pos_r = L - nq + jq
-                        assert [p for p, _ in got] == list(range(pos_r + 1)), (ei, h, jq, gi)
+                        assert [p for p, _ in got] == list(range(pos_r + 1)), (seq, h, jq, gi)
                         for p, kind in got:
                             want = "int8" if (fmt == 1 or _prot(p, L, S, R)) else "int4"
                             assert kind == want, (p, L)
