@@ -1050,15 +1050,16 @@ __global__ __launch_bounds__(64 * G) void merge_kernel(DecodeArgs a)
     float Ls = 0.f, O[NHV];
 #pragma unroll
     for (int hv = 0; hv < NHV; hv++) O[hv] = 0.f;
-    if (n >= 1 && n <= 16) {
-        // the usual case: every (m, l) and every output row are loaded before any is used (one
-        // memory round trip; rows past n repeat the last partial and get weight 0).  Same sums in
-        // the same order as the general loop below.
+    // the usual case: every (m, l) and every output row are loaded before any is used (one memory
+    // round trip; rows past n repeat the last partial and get weight 0).  Same sums in the same
+    // order as the general loop below.  NP = 4, 8 or 16 loads, the fewest that cover n.
+    auto fast = [&](auto NPC) {
+        constexpr int NP = decltype(NPC)::value;
         const float mj = lane < n ? ml[(int64_t)lane * G * 2] : -INFINITY;
         const float lj = lane < n ? ml[(int64_t)lane * G * 2 + 1] : 0.f;
-        float pv[16][NHV];
+        float pv[NP][NHV];
 #pragma unroll
-        for (int k = 0; k < 16; k++)
+        for (int k = 0; k < NP; k++)
 #pragma unroll
             for (int hv = 0; hv < NHV; hv++) pv[k][hv] = po[(int64_t)(k < n ? k : n - 1) * G * D + 64 * hv];
         M = wave_max_u(mj);
@@ -1066,7 +1067,7 @@ __global__ __launch_bounds__(64 * G) void merge_kernel(DecodeArgs a)
             const float fj = (mj == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mj - M);
             Ls = wave_sum_u(fj * lj);
 #pragma unroll
-            for (int k = 0; k < 16; k++) {
+            for (int k = 0; k < NP; k++) {
                 if (k < n) {
                     const float f = as_float((uint32_t)__builtin_amdgcn_readlane((int)as_uint(fj), k));
 #pragma unroll
@@ -1074,6 +1075,14 @@ __global__ __launch_bounds__(64 * G) void merge_kernel(DecodeArgs a)
                 }
             }
         }
+    };
+    if (n >= 1 && n <= 16) {
+        if (n <= 4)
+            fast(std::integral_constant<int, 4>{});
+        else if (n <= 8)
+            fast(std::integral_constant<int, 8>{});
+        else
+            fast(std::integral_constant<int, 16>{});
         M = -INFINITY; // the general loop below is skipped
     } else {
         for (int j0 = 0; j0 < n; j0 += 64) {
