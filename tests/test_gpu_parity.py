@@ -187,7 +187,9 @@ def test_decode_bf16_output(fmt, b):
 def test_decode_wave_counts():
     """The split kernel at explicit wave counts: one wave (every unit in one slice), counts that
     leave a workgroup partly empty (7, 13), and counts with slices shorter than a unit.  The
-    output must not depend on the partition beyond rounding order."""
+    output must not depend on the partition beyond rounding order.  Units then hold 1 to 64
+    partials, so the merge takes each of its paths (up to 4, 8 and 16 partials, and the general
+    loop): 500 waves alone give all four."""
     _print_case("wave counts")
     hq, hkv, d = 32, 8, 128
     lens = [1, 17, 100, 132, 133, 300, 1000]
@@ -195,7 +197,7 @@ def test_decode_wave_counts():
     ks, vs = zip(*[_kv(L, hkv, d, seed=3, idx=i) for i, L in enumerate(lens)])
     p.append(list(range(len(lens))), lens, torch.cat(ks).contiguous(), torch.cat(vs).contiguous())
     q = W.queries(len(lens), hq, d, seed=13, step=0, device="cuda")
-    for waves in (1, 7, 13, 64, 250, 0):
+    for waves in (1, 7, 13, 64, 250, 500, 0):
         p.gpu.set_decode_waves(waves)
         out, ref = p.decode(list(range(len(lens))), q)
         err = np.abs(out - ref).max()
