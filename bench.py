@@ -16,7 +16,8 @@ Prints ONE JSON line.
   >= 50 back-to-back decode-only launches (kernel-stamped HIP events on the call's stream), against
   the 8 TB/s HBM peak and against the probed streaming-read ceiling of the device.
 - baselines = the same workload with INT8-only and bf16 KV caches (pools of 4 distinct caches).
-- workloads = the Qwen3-8B layer (64 sequences, 1K-8K) and long context (8 x 131072).
+- workloads = the Qwen3-8B layer (64 sequences, 1K-8K), long context (8 x 131072) and one GPU's
+  share of the rollout regime under 8-way tensor parallelism by kv head (1 kv head, 4 q heads).
 - append = the append path alone, Hadamard block 128 against 1 (rotation overhead).
 - protection_cost = decode split time and bytes at (S, R) = (0, 0), (4, 0), (0, 128), (4, 128).
 - cpu_baseline = the CPU oracle's decode on a bounded sample of the same workload.
@@ -53,7 +54,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="rollout",
-                    choices=["rollout", "qwen3_8b_layer", "long_context", "tiny", "append", "multi_query"],
+                    choices=["rollout", "qwen3_8b_layer", "long_context", "rollout_tp8", "tiny", "append",
+                             "multi_query"],
                     help="decode workloads; 'append': the append path alone at Hadamard block 128 vs 1; "
                          "'multi_query': causal multi-query attention on the Qwen3-8B-shaped layer")
     ap.add_argument("--layers", type=int, default=0, help="layers per step (0: the workload's, 36 for rollout)")
@@ -780,7 +782,7 @@ def main():
         result["baselines"] = base
     if "workloads" in ex:
         wl = {}
-        for name in ("qwen3_8b_layer", "long_context"):
+        for name in ("qwen3_8b_layer", "long_context", "rollout_tp8"):
             if name == w.name:
                 continue
             log("workload %s" % name)

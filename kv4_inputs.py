@@ -68,6 +68,10 @@ WORKLOADS = {
                         length_args=(4096, 1.0, 256, 32768)),
     "long_context": Workload("long_context", 32, 8, 128, 4, 128, 128, 8, 4, 10.0, lengths_kind="fixed",
                              length_args=(131072,)),
+    # one GPU's share of the rollout regime under 8-way tensor parallelism by kv head: the same
+    # sequences and lengths, 1 kv head and its 4 query heads
+    "rollout_tp8": Workload("rollout_tp8", 4, 1, 128, 4, 128, 128, 256, 4, 10.0, layers=36, lengths_kind="lognormal",
+                            length_args=(4096, 1.0, 256, 32768)),
 }
 
 

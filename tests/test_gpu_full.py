@@ -119,6 +119,13 @@ def test_rollout_layer_full_size():
     _check_workload("rollout", lambda L: [int(np.argmin(L)), int(np.argmax(L)), 100])
 
 
+def test_rollout_tp8_full_size():
+    """One GPU's share of the rollout regime under 8-way tensor parallelism by kv head: 256
+    sequences with 1 kv head and 4 query heads, split over the bench's 2048 waves (8 per unit)."""
+    _print_case("rollout_tp8 full size")
+    _check_workload("rollout_tp8", lambda L: [int(np.argmin(L)), int(np.argmax(L)), 100])
+
+
 def test_long_context_full_size():
     _print_case("long_context full size")
     _check_workload("long_context", lambda L: [0, 3, len(L) - 1])

@@ -72,7 +72,7 @@ def test_ragged_batch(fmt, b, S, R):
     assert p.compare_cache(range(len(lens))) > 0
 
 
-@pytest.mark.parametrize("hq,hkv,d", [(8, 8, 128), (16, 8, 128), (8, 2, 64), (4, 4, 64)])
+@pytest.mark.parametrize("hq,hkv,d", [(8, 8, 128), (16, 8, 128), (8, 2, 64), (4, 4, 64), (4, 1, 128)])
 def test_group_and_dims(hq, hkv, d):
     _print_case("gqa", hq=hq, hkv=hkv, d=d)
     lens = [5, 200, 517]
