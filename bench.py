@@ -526,7 +526,8 @@ def mq_workload(device, n_q, steps, warmup, n_caches=4):
     hq, hkv, d, B = w.num_q_heads, w.num_kv_heads, w.head_dim, w.batch
     lens0 = w.lengths()
     prof_steps = 12
-    total = warmup + steps + prof_steps
+    ab_rounds, ab_steps = 4, 3  # per-wave against workgroup-shared INT4 steps, interleaved
+    total = warmup + steps + prof_steps + 2 * ab_rounds * ab_steps
     growth = (total // n_caches + 1) * n_q
     pages = sum(math.ceil((L + growth) / 16) for L in lens0) + B
     ch = W.outlier_channels(hkv, d, w.outlier_channels, w.seed)
@@ -581,6 +582,22 @@ def mq_workload(device, n_q, steps, warmup, n_caches=4):
         merge += c.profile_durations("mq_merge")
         app += c.profile_durations("append")
         c.profile_enable(False)
+    # the same steps with the INT4 steps per wave and shared by the workgroup, in A B B A order
+    G = hq // hkv
+    shares = -(-n_q * G // 16) % 4 == 0
+    ab = {True: [], False: []}
+    for r in range(ab_rounds):
+        for mode in ((True, False) if r % 2 == 0 else (False, True)):
+            for c in caches:
+                c.set_mq_share(mode)
+                c.profile_enable(True)
+            for _ in range(ab_steps):
+                one()
+            for c in caches:
+                ab[mode] += c.profile_durations("mq_split")
+                c.profile_enable(False)
+    for c in caches:
+        c.set_mq_share(True)
     split_s = statistics.fmean(split) * 1e-3
     bytes_launch, flops_launch = nbytes / prof_steps, flops / prof_steps
     gbps = bytes_launch / split_s / 1e9
@@ -592,7 +609,8 @@ def mq_workload(device, n_q, steps, warmup, n_caches=4):
     else:
         roof = {"bound": "mfma", "achieved": tflops, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": tflops / MFMA_F16_PEAK_TFLOPS}
-    roof.update({"traffic": None, "kernel": "mq_split_kernel<128,4,INT4_PROT>", "avg_launch_us": split_s * 1e6,
+    kname = "mq_split_shared_kernel<128,4,INT4_PROT>" if shares else "mq_split_kernel<128,4,INT4_PROT>"
+    roof.update({"traffic": None, "kernel": kname, "avg_launch_us": split_s * 1e6,
                  "median_launch_us": statistics.median(split) * 1e3,
                  "algorithmic_bytes_per_launch": bytes_launch, "algorithmic_flops_per_launch": flops_launch,
                  "achieved_GBps": gbps, "achieved_TFLOPs": tflops, "flops_per_byte": intensity})
@@ -605,7 +623,12 @@ def mq_workload(device, n_q, steps, warmup, n_caches=4):
                        "recent": w.num_recent, "hadamard_block": w.hadamard_block, "distinct_caches": n_caches},
             "roofline": roof,
             "step_breakdown_us": {"append": statistics.fmean(app) * 1e3, "mq_split": split_s * 1e6,
-                                  "mq_merge": statistics.fmean(merge) * 1e3}}
+                                  "mq_merge": statistics.fmean(merge) * 1e3},
+            "int4_steps_shared_by_workgroup": shares,
+            "split_us_shared_vs_per_wave": {
+                "shared": stats_us(ab[True]), "per_wave": stats_us(ab[False]),
+                "note": "interleaved A B B A rounds of %d steps; the shared kernel runs only when every "
+                        "sequence has a multiple of 4 row tiles, else both are the per-wave kernel" % ab_steps}}
 
 
 def write_traffic(fetch_dir, write_dir, workload, fmt="int4"):

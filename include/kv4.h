@@ -269,6 +269,12 @@ kv4_status kv4_set_decode_waves(kv4_cache_t h, int32_t waves);
  * (1000 - round1_permille) / 1000 of the call's steps (0 = one round).  The results do not depend
  * on it beyond rounding order. */
 kv4_status kv4_set_decode_rounds(kv4_cache_t h, int32_t round2_waves, int32_t round1_permille);
+/* Tuning: multi-query calls of the INT4+INT8 format in which every sequence has a multiple of 4
+ * row tiles (n_q * (hq / hkv) / 16 rounded up) let the four waves of a workgroup, which take
+ * four row tiles of the same pages, share each step's staged pages and spread operands
+ * (enable != 0, the default); 0 gives every wave its own.  The results are the same bits either
+ * way. */
+kv4_status kv4_set_mq_share(kv4_cache_t h, int32_t enable);
 
 /* Kernel timing (measurement of the hot path).  When enabled, each kernel a call launches on its
  * stream stamps a pair of HIP events from its own dispatch (start, stop), so a duration is that

@@ -125,6 +125,7 @@ def lib():
         L.kv4_free_pages.argtypes = [P, P]
         L.kv4_set_decode_waves.argtypes = [P, I32]
         L.kv4_set_decode_rounds.argtypes = [P, I32, I32]
+        L.kv4_set_mq_share.argtypes = [P, I32]
         L.kv4_profile_enable.argtypes = [P, I32]
         L.kv4_profile_read.argtypes = [P, P]
         L.kv4_profile_durations.argtypes = [P, I32, P, I32, P]
@@ -137,7 +138,7 @@ def lib():
                      "kv4_append", "kv4_append_rope", "kv4_seq_free", "kv4_decode_workspace_size", "kv4_decode_attention",
                      "kv4_decode_attention_bf16", "kv4_decode_attention_noalloc",
                      "kv4_multi_query_workspace_size", "kv4_multi_query_attention",
-                     "kv4_seq_length", "kv4_block_table", "kv4_free_pages", "kv4_set_decode_waves", "kv4_set_decode_rounds",
+                     "kv4_seq_length", "kv4_block_table", "kv4_free_pages", "kv4_set_decode_waves", "kv4_set_decode_rounds", "kv4_set_mq_share",
                      "kv4_profile_enable", "kv4_profile_read", "kv4_profile_durations", "kv4_hbm_probe"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -413,6 +414,9 @@ class Cache:
 
     def set_decode_rounds(self, round2_waves: int, round1_permille: int = 1000):
         _check(lib().kv4_set_decode_rounds(self._h, int(round2_waves), int(round1_permille)), self._h)
+
+    def set_mq_share(self, enable: bool):
+        _check(lib().kv4_set_mq_share(self._h, int(bool(enable))), self._h)
 
     def profile_enable(self, enable: bool = True):
         _check(lib().kv4_profile_enable(self._h, 1 if enable else 0), self._h)

@@ -177,6 +177,7 @@ struct kv4_cache {
     int mq_resident_waves = 2048; // multi-query split waves resident at once
     int decode_waves = 0; // 0: automatic
     int round2_waves = 0; // decode split: waves of a second round (0: one round)
+    int mq_share = 1;     // multi-query split: workgroup-shared INT4 steps where the row tiles allow
     int round1_permille = 1000; // share of the steps in the first round when there is a second
     float cb = 1.0f;
     void* scratch = nullptr;                // this device's decode scratch (kDecodeScratchBytes)
@@ -779,6 +780,13 @@ kv4_status kv4_multi_query_attention(kv4_cache_t h, int32_t n_seqs, const int32_
     a.block = h->st.cfg.block;
     a.int8_tiles = h->sizes.int8_tiles;
     a.n8 = kv4::mq_int8_steps(h->st.cfg);
+    // the shared kernel takes row tiles 4k .. 4k + 3 of one chunk per workgroup
+    a.share = 0;
+    if (h->mq_share && h->st.cfg.format == kv4::FMT_INT4_PROT) {
+        a.share = 1;
+        for (const kv4::MqEntry& en : plan.entries)
+            if ((((int64_t)en.nq * G + kv4::kMqRows - 1) / kv4::kMqRows) % 4 != 0) a.share = 0;
+    }
     a.cb = h->cb;
     const double sc = scale > 0.f ? (double)scale : 1.0 / std::sqrt((double)D);
     a.scale_log2 = (float)(sc * 1.4426950408889634);
@@ -836,6 +844,13 @@ kv4_status kv4_set_decode_rounds(kv4_cache_t h, int32_t round2_waves, int32_t ro
         return fail(h, KV4_ERR_INVALID_ARGUMENT, "bad argument");
     h->round2_waves = round2_waves;
     h->round1_permille = round1_permille;
+    return KV4_OK;
+}
+
+kv4_status kv4_set_mq_share(kv4_cache_t h, int32_t enable)
+{
+    if (!h) return fail(nullptr, KV4_ERR_INVALID_ARGUMENT, "null handle");
+    h->mq_share = enable != 0;
     return KV4_OK;
 }
 

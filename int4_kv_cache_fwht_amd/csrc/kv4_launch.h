@@ -83,6 +83,9 @@ struct MqArgs {
     int64_t page_block;
     int64_t int8_tile;
     int n_entries, tasks, groups, spc;
+    // INT4_PROT: the four waves of a workgroup share their INT4 steps (every entry's row-tile
+    // count is a multiple of 4)
+    int share;
     int hq, hkv, max_pps, sinks, recent, block, int8_tiles, n8;
     float cb;         // fl32(1/sqrt(block))
     float scale_log2; // softmax scale * log2(e)

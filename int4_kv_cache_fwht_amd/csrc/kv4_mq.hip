@@ -190,6 +190,18 @@ struct MqWave {
     static constexpr int CPB = (IB + 1023) / 1024; // 1 KB copy instructions per page block
     static constexpr int SB = 1024 * CPB;          // LDS bytes of a staged page block (padded)
     static constexpr int STAGE = 2 * SB;           // LDS bytes of one staged INT4 step (two blocks)
+    static constexpr int RING = kMqStages * STAGE; // a wave's own stage ring
+    // Workgroup-shared INT4 steps (the four waves take four row tiles of one chunk): one stage ring
+    // for the workgroup, and each wave spreads a quarter of a step's operands into LDS for all four.
+    static constexpr int NOPS = NCB;               // shared operands of a step: the value blocks
+    static constexpr int QOPS = NOPS / 4;          // operands a wave spreads
+    static constexpr int NCOPY = 2 * CPB;          // copy instructions of a step
+    static constexpr int PERW = (NCOPY + 3) / 4;   // copies a wave issues per step
+    static constexpr int SH_STAGES = 4;            // shared ring: steps s .. s + 3 (indices taken & 3)
+    static constexpr int SH_RING = SH_STAGES * STAGE;
+    static constexpr int SPR = NOPS * 64 * 16;     // one step's spread operands
+    static constexpr int SH_LDS = SH_RING + 2 * SPR;
+    static_assert(NOPS % 4 == 0, "the operands split evenly over four waves");
 
     // One step's operands for this lane.  INT8 buffers hold twice the key and value bytes.
     template <bool IS8>
@@ -211,7 +223,9 @@ struct MqWave {
     uint32_t pstride;     // bytes from one page to the next (all kv heads' blocks)
     int p0, p1;          // INT4 page range (INT4_PROT) or page count (INT8 format: p1)
     float m_ref = -__builtin_inff(), lsum = 0.f, zsum = 0.f, Ar = 0.f, Br = 0.f;
-    __attribute__((address_space(3))) uint8_t* ring; // this wave's kMqStages INT4 stage buffers
+    __attribute__((address_space(3))) uint8_t* ring; // kMqStages INT4 stage buffers (the wave's or the workgroup's)
+    __attribute__((address_space(3))) uint8_t* spr;  // shared steps: the spread operands [NOPS][64 lanes][16 B]
+    int wv = 0;          // shared steps: wave index in the workgroup
     uint32_t k6400;      // 0x64006400 in a vector register (identity DPP move: not a literal)
     float m1;            // -1 in a vector register (the same)
     u32x4 qhi[KS], qlo[KS];
@@ -446,10 +460,33 @@ struct MqWave {
         }
     }
 
-    // One step.  FULL: every position of the step is readable and at or before every row's own
-    // position (wave-uniform), so no per-position test is made.
+    // One step from a buffer of raw codes: the operands are spread as the products need them.
     template <bool IS8, bool FULL>
-    __device__ void compute(const Buf<IS8>& b, int s)
+    __device__ __forceinline__ void compute(const Buf<IS8>& b, int s)
+    {
+        constexpr int MID = IS8 ? 128 : 8;
+        compute_with<IS8, FULL>(
+            [&](int t, int j) {
+                if constexpr (IS8)
+                    return spread_int8(b.k[t][2 * j], b.k[t][2 * j + 1]);
+                else
+                    return spread_int4_x16(b.k[t][j]);
+            },
+            [&](int c) {
+                if constexpr (IS8)
+                    return centre<MID>(spread_int8(b.v[c][0], b.v[c][1]));
+                else
+                    return spread_centre_int4<MID>(b.v[c][0], k6400);
+            },
+            b.sc, s);
+    }
+
+    // One step.  FULL: every position of the step is readable and at or before every row's own
+    // position (wave-uniform), so no per-position test is made.  kop(t, j) gives the key operand of
+    // tile t and k-step j (spread codes), vop(c) the value operand of column block c (centred
+    // codes), sc the step's 16 scale words of this lane.
+    template <bool IS8, bool FULL, typename KOp, typename VOp>
+    __device__ __forceinline__ void compute_with(KOp kop, VOp vop, const uint32_t (&sc)[16], int s)
     {
         constexpr int MID = IS8 ? 128 : 8;
         int pos[8];
@@ -458,8 +495,8 @@ struct MqWave {
         float4_t sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < KS; j++) {
-            const u32x4 ka = IS8 ? spread_int8(b.k[0][2 * j], b.k[0][2 * j + 1]) : spread_int4_x16(b.k[0][j]);
-            const u32x4 kb = IS8 ? spread_int8(b.k[1][2 * j], b.k[1][2 * j + 1]) : spread_int4_x16(b.k[1][j]);
+            const u32x4 ka = kop(0, j);
+            const u32x4 kb = kop(1, j);
             const u32x4 qh = IS8 ? odd_x16(qhi[j]) : qhi[j];
             const u32x4 ql = IS8 ? odd_x16(qlo[j]) : qlo[j];
             sa = mfma16x32(ka, qh, sa);
@@ -478,7 +515,7 @@ struct MqWave {
 #pragma unroll
         for (int t = 0; t < 8; t++) {
             const float r = t < 4 ? sa[t] : sb[t - 4];
-            const uint32_t d0 = b.sc[2 * t], d1 = b.sc[2 * t + 1];
+            const uint32_t d0 = sc[2 * t], d1 = sc[2 * t + 1];
             st[t] = fmaf(lo_half(d0), r * Ar, fmaf(hi_half(d0), Br, 0.f));
             ok[t] = FULL || pos[t] <= pos_r;
             smax = ok[t] ? fmaxf(smax, st[t]) : smax;
@@ -486,9 +523,9 @@ struct MqWave {
         }
         if (FULL) {
             // every slot read: the largest s_V pattern by 16-bit maxima of the low halves
-            u16x2 mv = as_u16x2(b.sc[1]);
+            u16x2 mv = as_u16x2(sc[1]);
 #pragma unroll
-            for (int t = 1; t < 8; t++) mv = __builtin_elementwise_max(mv, as_u16x2(b.sc[2 * t + 1]));
+            for (int t = 1; t < 8; t++) mv = __builtin_elementwise_max(mv, as_u16x2(sc[2 * t + 1]));
             svmax = mv.x;
         }
         float wmax = smax + (float)(svmax >> 10);
@@ -513,7 +550,7 @@ struct MqWave {
         const float m27 = m_ref - 27.f;
 #pragma unroll
         for (int t = 0; t < 8; t++) {
-            const uint32_t d1 = b.sc[2 * t + 1];
+            const uint32_t d1 = sc[2 * t + 1];
             // unread slots hold unspecified bytes (their scales may be inf / NaN): select, never
             // multiply them by zero
             const float p = ok[t] ? __builtin_amdgcn_exp2f(st[t] - m27) : 0.f;
@@ -525,8 +562,7 @@ struct MqWave {
         split_hilo_rtz(P, phi, plo, m1);
 #pragma unroll
         for (int c = 0; c < NCB; c++) {
-            const u32x4 bv = IS8 ? centre<MID>(spread_int8(b.v[c][0], b.v[c][1]))
-                                 : spread_centre_int4<MID>(b.v[c][0], k6400);
+            const u32x4 bv = vop(c);
             acc[c] = mfma16x32(phi, bv, acc[c]);
             acc[c] = mfma16x32(plo, bv, acc[c]);
         }
@@ -589,6 +625,142 @@ struct MqWave {
         wait_vmcnt<0>();
     }
 
+    // ---- INT4 steps shared by the four waves of a workgroup (row tiles 4k .. 4k + 3 of one
+    // (entry, kv head, chunk)): the same pages, the same steps [s0, s1), the same barriers. ----
+
+    // The copies of a step into the workgroup's stage st: wave wv issues copies wv and wv + 4 of the
+    // step's NCOPY (the last one repeated where the count runs out: the same bytes to the same
+    // place), so every wave issues PERW copies per step.
+    __device__ __forceinline__ void stage_copy_sh(uint32_t pa, uint32_t pb, int st) const
+    {
+        __attribute__((address_space(3))) uint8_t* dst = ring + st * STAGE;
+#pragma unroll
+        for (int m = 0; m < PERW; m++) {
+            const int k = min(wv + 4 * m, NCOPY - 1);
+            const int x = k / CPB, i = k - x * CPB;
+            const uint8_t* src = hbase + (uint64_t)(x ? pb : pa) * pstride;
+            int off = 1024 * i + 16 * lane;
+            if (1024 * (i + 1) > IB) off = off < IB ? off : IB - 128 + 16 * (lane & 7);
+            __builtin_amdgcn_global_load_lds((const void*)(src + off),
+                                             (__attribute__((address_space(3))) void*)(dst + x * SB + 1024 * i), 16, 0,
+                                             0);
+        }
+    }
+
+    // This wave's quarter of the step's value operands (column blocks QOPS wv ..), spread from
+    // stage st into operand area buf (each lane's code words sit where stage_read finds them).
+    // The key operands stay per wave: their spread costs 5 VALU per 8 codes against 11 for the
+    // centred values, for the same LDS bytes.
+    __device__ __forceinline__ void spread_quarter(int st, int buf) const
+    {
+        const __attribute__((address_space(3))) uint8_t* vp =
+            ring + st * STAGE + (g < 2 ? 0 : SB) + 8 * D + (16 * QOPS * wv + n) * 8 + 4 * (g & 1);
+        __attribute__((address_space(3))) u32x4* dst =
+            (__attribute__((address_space(3))) u32x4*)(spr + buf * SPR) + (QOPS * wv) * 64 + lane;
+        uint32_t w[QOPS];
+#pragma unroll
+        for (int q = 0; q < QOPS; q++) w[q] = *(const __attribute__((address_space(3))) uint32_t*)(vp + 128 * q);
+#pragma unroll
+        for (int q = 0; q < QOPS; q++) dst[q * 64] = spread_centre_int4<8>(w[q], k6400);
+    }
+
+    __device__ __forceinline__ void compute_sh(int st, int buf, int s)
+    {
+        const __attribute__((address_space(3))) uint8_t* vp = ring + st * STAGE + (g < 2 ? 0 : SB);
+        uint32_t sc[16];
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const u32x4 w = *(const __attribute__((address_space(3))) u32x4*)(vp + 16 * D + 64 * (g & 1) + 16 * j);
+#pragma unroll
+            for (int i = 0; i < 4; i++) sc[4 * j + i] = w[i];
+        }
+        // key code words of this lane, as stage_read reads them
+        uint32_t kw[2][KS];
+        {
+            const int kslot = 8 * ((n >> 2) & 1) + (n & 3);
+            const __attribute__((address_space(3))) uint8_t* kp = ring + st * STAGE + (n < 8 ? 0 : SB) + kslot * 16;
+            if constexpr (D == 128) {
+                kp += 256 * g;
+#pragma unroll
+                for (int t = 0; t < 2; t++) {
+                    const u32x4 w = *(const __attribute__((address_space(3))) u32x4*)(kp + 64 * t);
+#pragma unroll
+                    for (int j = 0; j < 4; j++) kw[t][j] = w[j];
+                }
+            } else {
+                kp += 256 * (g >> 1) + 8 * (g & 1);
+#pragma unroll
+                for (int t = 0; t < 2; t++) {
+                    const u32x2 w = *(const __attribute__((address_space(3))) u32x2*)(kp + 64 * t);
+                    kw[t][0] = w[0];
+                    kw[t][1] = w[1];
+                }
+            }
+        }
+        const __attribute__((address_space(3))) u32x4* op =
+            (const __attribute__((address_space(3))) u32x4*)(spr + buf * SPR) + lane;
+        auto kop = [&](int t, int j) { return spread_int4_x16(kw[t][j]); };
+        auto vop = [&](int c) { return op[c * 64]; };
+        if (interior(s))
+            compute_with<false, true>(kop, vop, sc, s);
+        else
+            compute_with<false, false>(kop, vop, sc, s);
+    }
+
+    // s_waitcnt vmcnt(N) lgkmcnt(0), then the workgroup barrier, as one statement the compiler
+    // does not move memory accesses across (a fence would also wait for the copies in flight).
+    template <int N>
+    __device__ __forceinline__ static void barrier_vm()
+    {
+        static_assert(N >= 0 && N < 16, "small vmcnt");
+        if constexpr (N == 0)
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        else if constexpr (N == 1)
+            asm volatile("s_waitcnt vmcnt(1) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        else if constexpr (N == 2)
+            asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        else if constexpr (N == 4)
+            asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        else
+            static_assert(N <= 2 || N == 4, "add the count");
+    }
+    __device__ __forceinline__ static void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+    // One barrier per step, with the spread one step ahead of the products.  Before iteration i
+    // (step s = s0 + i) the ring holds steps s .. s + 2 (s + 1, s + 2 possibly in flight) and
+    // operand area i % 2 holds step s spread.  Iteration i: wait for this wave's copies of step
+    // s + 1; barrier (every copy of s + 1 has landed, area i % 2 is complete, and every wave is done
+    // with step s - 1: its stage and area (i + 1) % 2 are free); copy step s + 3 into the freed
+    // stage; spread this wave's quarter of step s + 1 into area (i + 1) % 2; compute step s.  Past
+    // s1 - 1 the copies repeat the last step and their spreads are never read.  [s0, s1) is the
+    // same for the four waves, so every wave passes the same barriers.
+    __device__ void run4_sh(int s0, int s1)
+    {
+        if (s0 >= s1) return;
+        uint32_t pa, pb;
+#pragma unroll
+        for (int j = 0; j < SH_STAGES - 1; j++) {
+            step_pages(min(s0 + j, s1 - 1), pa, pb);
+            stage_copy_sh(pa, pb, j);
+        }
+        step_pages(min(s0 + SH_STAGES - 1, s1 - 1), pa, pb);
+        __builtin_amdgcn_sched_barrier(0);
+        barrier_vm<(SH_STAGES - 2) * PERW>();
+        __builtin_amdgcn_sched_barrier(0);
+        spread_quarter(0, 0);
+        for (int i = 0; i < s1 - s0; i++) {
+            __builtin_amdgcn_sched_barrier(0);
+            barrier_vm<(SH_STAGES - 3) * PERW>();
+            __builtin_amdgcn_sched_barrier(0);
+            stage_copy_sh(pa, pb, (i + 3) & 3);
+            step_pages(min(s0 + i + SH_STAGES, s1 - 1), pa, pb);
+            spread_quarter((i + 1) & 3, (i + 1) & 1);
+            compute_sh(i & 3, i & 1, s0 + i);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        barrier_vm<0>();
+    }
+
     __device__ void finish(int task)
     {
         lsum += lane_xor16(lsum);
@@ -624,13 +796,14 @@ __device__ __forceinline__ int xcd_grouped_block(int b, int nb)
     return (slot >> 2) * 32 + xcd * 4 + (slot & 3);
 }
 
-template <int D, int G, int FMT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void mq_split_kernel(MqArgs a)
+// The task's wave: entry, kv head, chunk and row tile of task `wave`, then its steps.  SH: the
+// INT4 steps are shared by the workgroup's four waves (tasks 4k .. 4k + 3: row tiles of one
+// chunk), through `ring` (the workgroup's stage ring) and `spr` (its operand area).
+template <int D, int G, int FMT, bool SH>
+__device__ __forceinline__ void mq_split_task(const MqArgs& a, int wave, int lane, int wv,
+                                              __attribute__((address_space(3))) uint8_t* ring,
+                                              __attribute__((address_space(3))) uint8_t* spr)
 {
-    const int wave = xcd_grouped_block((int)blockIdx.x, (int)gridDim.x) * 4 + (int)(threadIdx.x >> 6);
-    if (wave >= a.tasks) return;
-    const int lane = (int)(threadIdx.x & 63);
-    __shared__ __align__(16) uint8_t mq_ring[4][kMqStages * 2 * 1024 * ((16 * D + 128 + 1023) / 1024)];
     const int lo = mq_find_entry<false>(a, wave, lane);
     MqEntry e;
     e.seq = mq_uniform(&a.entries[lo].seq);
@@ -648,7 +821,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     const int rt = local - chunk * nrt;
 
     MqWave<D, G, FMT> W(a, lane);
-    W.ring = (__attribute__((address_space(3))) uint8_t*)mq_ring[__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)];
+    W.ring = ring;
+    W.spr = spr;
+    W.wv = wv;
     W.seq = e.seq;
     W.L = e.len;
     W.head = head;
@@ -673,8 +848,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     const int n8 = FMT == FMT_INT8 ? e.steps : a.n8;
     W.prologue(e, rt);
     W.run8(s0, s1 < n8 ? s1 : n8);
-    if (FMT == FMT_INT4_PROT) W.run4(s0 > n8 ? s0 : n8, s1);
+    if (FMT == FMT_INT4_PROT) {
+        if constexpr (SH)
+            W.run4_sh(s0 > n8 ? s0 : n8, s1);
+        else
+            W.run4(s0 > n8 ? s0 : n8, s1);
+    }
     W.finish(wave);
+}
+
+template <int D, int G, int FMT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void mq_split_kernel(MqArgs a)
+{
+    const int wave = xcd_grouped_block((int)blockIdx.x, (int)gridDim.x) * 4 + (int)(threadIdx.x >> 6);
+    if (wave >= a.tasks) return;
+    const int lane = (int)(threadIdx.x & 63);
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    __shared__ __align__(16) uint8_t mq_ring[4][MqWave<D, G, FMT>::RING];
+    mq_split_task<D, G, FMT, false>(a, wave, lane, wv, (__attribute__((address_space(3))) uint8_t*)mq_ring[wv], nullptr);
+}
+
+// Workgroup-shared INT4 steps: launched only when every entry's row-tile count is a multiple of 4,
+// so that a.tasks is too and the four waves of a workgroup take row tiles 4k .. 4k + 3 of one
+// (entry, kv head, chunk): all four run the same steps and pass the same barriers, and no wave of
+// a launched workgroup leaves early.
+template <int D, int G, int FMT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void mq_split_shared_kernel(MqArgs a)
+{
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wave = xcd_grouped_block((int)blockIdx.x, (int)gridDim.x) * 4 + wv;
+    const int lane = (int)(threadIdx.x & 63);
+    __shared__ __align__(16) uint8_t mq_sh[MqWave<D, G, FMT>::SH_LDS];
+    __attribute__((address_space(3))) uint8_t* base = (__attribute__((address_space(3))) uint8_t*)mq_sh;
+    mq_split_task<D, G, FMT, true>(a, wave, lane, wv, base, base + MqWave<D, G, FMT>::SH_RING);
 }
 
 // Merge waves: one per (row tile, RQ of its rows); lane l holds output dims DPM l .. DPM l + DPM - 1.
@@ -825,6 +1031,10 @@ template <int D, int G, int FMT>
 hipError_t split_dispatch(const MqArgs& a, hipStream_t stream, const KernelTimer& tm)
 {
     const int blocks = (a.tasks + 3) / 4;
+    if (FMT == FMT_INT4_PROT && a.share) {
+        if (a.tasks % 4 != 0) return hipErrorInvalidValue; // the shared kernel needs whole workgroups
+        return launch_kernel(mq_split_shared_kernel<D, G, FMT>, dim3(blocks), dim3(256), stream, tm, a);
+    }
     return launch_kernel(mq_split_kernel<D, G, FMT>, dim3(blocks), dim3(256), stream, tm, a);
 }
 

@@ -111,7 +111,7 @@ def _check_workload(name, sample_fn, positions_per_seq=12, mq_rows=(4,)):
 
 def test_qwen3_8b_layer_full_size():
     _print_case("qwen3_8b_layer full size")
-    _check_workload("qwen3_8b_layer", lambda L: [int(np.argmin(L)), int(np.argmax(L)), 17, 40], mq_rows=(4, 16))
+    _check_workload("qwen3_8b_layer", lambda L: [int(np.argmin(L)), int(np.argmax(L)), 17, 40], mq_rows=(4, 16, 64))
 
 
 def test_rollout_layer_full_size():

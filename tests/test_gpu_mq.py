@@ -128,6 +128,37 @@ def test_mq_full_size_sampled():
         assert err <= TOL
 
 
+@pytest.mark.parametrize("hq,hkv,d,b,S,R,unit", [
+    (32, 8, 128, 128, 4, 128, 16),   # G 4: a row tile is 4 query positions, 4 tiles per 16 rows
+    (32, 8, 128, 1, 0, 0, 16),
+    (32, 8, 128, 32, 4, 32, 16),
+    (16, 8, 128, 128, 4, 128, 32),   # G 2
+    (8, 8, 128, 64, 0, 16, 64),      # G 1
+    (8, 2, 64, 64, 4, 32, 16),       # D 64: one copy per wave and step
+])
+def test_mq_shared_steps(hq, hkv, d, b, S, R, unit):
+    """Every sequence with a multiple of 4 row tiles: the four waves of a workgroup share each INT4
+    step's staged pages and spread operands.  The output equals the unshared kernel's bit for bit
+    and the oracle within the tolerance, over ragged lengths and several chunks per sequence."""
+    _print_case("mq_shared", hq=hq, hkv=hkv, d=d, b=b, S=S, R=R)
+    lens = [unit + 1, 100, 257, 300, 1000, 2500]
+    nqs = [unit, unit * (100 // unit), unit * 2, unit, unit * 4, unit * 3]
+    p = Pair(hq, hkv, d, num_pages=1024, max_seqs=8, max_pps=192, S=S, R=R, b=b)
+    _fill(p, lens, hkv, d, seed=41)
+    q = _q(sum(nqs), hq, d, seed=42)
+    order = [3, 0, 5, 1, 4, 2]
+    qo = _reorder(q, nqs, order)
+    ids, nq = order, [nqs[i] for i in order]
+    p.gpu.set_mq_share(False)
+    own = p.gpu.multi_query_attention(ids, nq, qo).cpu().numpy()
+    p.gpu.set_mq_share(True)
+    out, ref = p.multi(ids, nq, qo)
+    assert np.array_equal(out.astype(np.float32), own), "shared and per-wave steps differ"
+    err = np.abs(out - ref).max()
+    print("mq shared max-abs", err)
+    assert err <= TOL
+
+
 def test_mq_errors():
     _print_case("mq_errors")
     p = Pair(8, 2, 64, num_pages=64, max_seqs=4, max_pps=16, S=4, R=16, b=64)
