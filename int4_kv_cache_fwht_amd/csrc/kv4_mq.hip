@@ -460,39 +460,98 @@ struct MqWave {
         }
     }
 
-    // One step from a buffer of raw codes: the operands are spread as the products need them.
-    template <bool IS8, bool FULL>
-    __device__ __forceinline__ void compute(const Buf<IS8>& b, int s)
-    {
-        constexpr int MID = IS8 ? 128 : 8;
-        compute_with<IS8, FULL>(
-            [&](int t, int j) {
-                if constexpr (IS8)
-                    return spread_int8(b.k[t][2 * j], b.k[t][2 * j + 1]);
-                else
-                    return spread_int4_x16(b.k[t][j]);
-            },
-            [&](int c) {
-                if constexpr (IS8)
-                    return centre<MID>(spread_int8(b.v[c][0], b.v[c][1]));
-                else
-                    return spread_centre_int4<MID>(b.v[c][0], k6400);
-            },
-            b.sc, s);
-    }
-
     // One step.  FULL: every position of the step is readable and at or before every row's own
-    // position (wave-uniform), so no per-position test is made.  kop(t, j) gives the key operand of
-    // tile t and k-step j (spread codes), vop(c) the value operand of column block c (centred
-    // codes), sc the step's 16 scale words of this lane.
-    template <bool IS8, bool FULL, typename KOp, typename VOp>
-    __device__ __forceinline__ void compute_with(KOp kop, VOp vop, const uint32_t (&sc)[16], int s)
+    // position (wave-uniform), so no per-position test is made.
+    template <bool IS8, bool FULL>
+    __device__ void compute(const Buf<IS8>& b, int s)
     {
         constexpr int MID = IS8 ? 128 : 8;
         int pos[8];
         if (!FULL) positions<IS8>(s, pos);
         // S^T for the two tiles
         float4_t sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < KS; j++) {
+            const u32x4 ka = IS8 ? spread_int8(b.k[0][2 * j], b.k[0][2 * j + 1]) : spread_int4_x16(b.k[0][j]);
+            const u32x4 kb = IS8 ? spread_int8(b.k[1][2 * j], b.k[1][2 * j + 1]) : spread_int4_x16(b.k[1][j]);
+            const u32x4 qh = IS8 ? odd_x16(qhi[j]) : qhi[j];
+            const u32x4 ql = IS8 ? odd_x16(qlo[j]) : qlo[j];
+            sa = mfma16x32(ka, qh, sa);
+            sb = mfma16x32(kb, qh, sb);
+            sa = mfma16x32(ka, ql, sa);
+            sb = mfma16x32(kb, ql, sb);
+        }
+        // fp16 scales enter the fp32 arithmetic as fma operands (v_fma_mix_f32: no conversions).
+        // The reference bound uses one exponent per lane: the largest s_V of the lane's readable
+        // positions (positive fp16 patterns order like their values), so st + e_lane bounds
+        // st + log2 s_V + 1 for each of them.
+        float st[8];
+        bool ok[8];
+        float smax = -__builtin_inff();
+        uint32_t svmax = 0;
+#pragma unroll
+        for (int t = 0; t < 8; t++) {
+            const float r = t < 4 ? sa[t] : sb[t - 4];
+            const uint32_t d0 = b.sc[2 * t], d1 = b.sc[2 * t + 1];
+            st[t] = fmaf(lo_half(d0), r * Ar, fmaf(hi_half(d0), Br, 0.f));
+            ok[t] = FULL || pos[t] <= pos_r;
+            smax = ok[t] ? fmaxf(smax, st[t]) : smax;
+            if (!FULL) svmax = ok[t] ? max(svmax, d1 & 0xFFFFu) : svmax;
+        }
+        if (FULL) {
+            // every slot read: the largest s_V pattern by 16-bit maxima of the low halves
+            u16x2 mv = as_u16x2(b.sc[1]);
+#pragma unroll
+            for (int t = 1; t < 8; t++) mv = __builtin_elementwise_max(mv, as_u16x2(b.sc[2 * t + 1]));
+            svmax = mv.x;
+        }
+        float wmax = smax + (float)(svmax >> 10);
+        wmax = fmaxf(wmax, lane_xor16(wmax));
+        wmax = max_xor32(wmax);
+        const bool need = wmax > m_ref + kMqTau;
+        if (__builtin_amdgcn_ballot_w64(need)) {
+            const float f = need ? __builtin_amdgcn_exp2f(m_ref - wmax) : 1.f;
+            if (need) m_ref = wmax;
+            lsum *= f;
+            zsum *= f;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const float fr = __shfl(f, 4 * g + i, 64);
+#pragma unroll
+                for (int c = 0; c < NCB; c++) acc[c][i] *= fr;
+            }
+        }
+        // p is carried as p * 2^27 (lsum, zsum too; undone in finish): P = p * 2^27 * s_V is then
+        // one fma, and P < 2^14 by the reference rule
+        float P[8];
+        const float m27 = m_ref - 27.f;
+#pragma unroll
+        for (int t = 0; t < 8; t++) {
+            const uint32_t d1 = b.sc[2 * t + 1];
+            // unread slots hold unspecified bytes (their scales may be inf / NaN): select, never
+            // multiply them by zero
+            const float p = ok[t] ? __builtin_amdgcn_exp2f(st[t] - m27) : 0.f;
+            lsum += p;
+            zsum = ok[t] ? fmaf(p, fmaf(lo_half(d1), (float)MID, hi_half(d1)), zsum) : zsum;
+            P[t] = ok[t] ? fmaf(lo_half(d1), p, 0.f) : 0.f;
+        }
+        u32x4 phi, plo;
+        split_hilo_rtz(P, phi, plo, m1);
+#pragma unroll
+        for (int c = 0; c < NCB; c++) {
+            const u32x4 bv = IS8 ? centre<MID>(spread_int8(b.v[c][0], b.v[c][1]))
+                                 : spread_centre_int4<MID>(b.v[c][0], k6400);
+            acc[c] = mfma16x32(phi, bv, acc[c]);
+            acc[c] = mfma16x32(plo, bv, acc[c]);
+        }
+    }
+
+    // S^T of a step for the two tiles of 16 positions
+    template <bool IS8, typename KOp>
+    __device__ __forceinline__ void qk(KOp kop, float4_t& sa, float4_t& sb) const
+    {
+        sa = (float4_t){0.f, 0.f, 0.f, 0.f};
+        sb = (float4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < KS; j++) {
             const u32x4 ka = kop(0, j);
@@ -504,6 +563,17 @@ struct MqWave {
             sa = mfma16x32(ka, ql, sa);
             sb = mfma16x32(kb, ql, sb);
         }
+    }
+
+    // The rest of a step, from its S^T: scores, online softmax, O += P' V (the arithmetic of
+    // compute() after its products, for operands that come from the workgroup's shared area).
+    template <bool IS8, bool FULL, typename VOp>
+    __device__ __forceinline__ void softmax_pv(const float4_t& sa, const float4_t& sb, VOp vop,
+                                               const uint32_t (&sc)[16], int s)
+    {
+        constexpr int MID = IS8 ? 128 : 8;
+        int pos[8];
+        if (!FULL) positions<IS8>(s, pos);
         // fp16 scales enter the fp32 arithmetic as fma operands (v_fma_mix_f32: no conversions).
         // The reference bound uses one exponent per lane: the largest s_V of the lane's readable
         // positions (positive fp16 patterns order like their values), so st + e_lane bounds
@@ -664,8 +734,38 @@ struct MqWave {
         for (int q = 0; q < QOPS; q++) dst[q * 64] = spread_centre_int4<8>(w[q], k6400);
     }
 
+    // S^T of the step in stage st (its key codes, spread by this wave)
+    __device__ __forceinline__ void qk_sh(int st, float4_t& sa, float4_t& sb) const
+    {
+        uint32_t kw[2][KS];
+        const int kslot = 8 * ((n >> 2) & 1) + (n & 3);
+        const __attribute__((address_space(3))) uint8_t* kp = ring + st * STAGE + (n < 8 ? 0 : SB) + kslot * 16;
+        if constexpr (D == 128) {
+            kp += 256 * g;
+#pragma unroll
+            for (int t = 0; t < 2; t++) {
+                const u32x4 w = *(const __attribute__((address_space(3))) u32x4*)(kp + 64 * t);
+#pragma unroll
+                for (int j = 0; j < 4; j++) kw[t][j] = w[j];
+            }
+        } else {
+            kp += 256 * (g >> 1) + 8 * (g & 1);
+#pragma unroll
+            for (int t = 0; t < 2; t++) {
+                const u32x2 w = *(const __attribute__((address_space(3))) u32x2*)(kp + 64 * t);
+                kw[t][0] = w[0];
+                kw[t][1] = w[1];
+            }
+        }
+        qk<false>([&](int t, int j) { return spread_int4_x16(kw[t][j]); }, sa, sb);
+    }
+
+    // Step s: S^T from its key codes in stage st, then the softmax and P V with the scales from
+    // stage st and the value operands from area buf.
     __device__ __forceinline__ void compute_sh(int st, int buf, int s)
     {
+        float4_t sa, sb;
+        qk_sh(st, sa, sb);
         const __attribute__((address_space(3))) uint8_t* vp = ring + st * STAGE + (g < 2 ? 0 : SB);
         uint32_t sc[16];
 #pragma unroll
@@ -674,37 +774,13 @@ struct MqWave {
 #pragma unroll
             for (int i = 0; i < 4; i++) sc[4 * j + i] = w[i];
         }
-        // key code words of this lane, as stage_read reads them
-        uint32_t kw[2][KS];
-        {
-            const int kslot = 8 * ((n >> 2) & 1) + (n & 3);
-            const __attribute__((address_space(3))) uint8_t* kp = ring + st * STAGE + (n < 8 ? 0 : SB) + kslot * 16;
-            if constexpr (D == 128) {
-                kp += 256 * g;
-#pragma unroll
-                for (int t = 0; t < 2; t++) {
-                    const u32x4 w = *(const __attribute__((address_space(3))) u32x4*)(kp + 64 * t);
-#pragma unroll
-                    for (int j = 0; j < 4; j++) kw[t][j] = w[j];
-                }
-            } else {
-                kp += 256 * (g >> 1) + 8 * (g & 1);
-#pragma unroll
-                for (int t = 0; t < 2; t++) {
-                    const u32x2 w = *(const __attribute__((address_space(3))) u32x2*)(kp + 64 * t);
-                    kw[t][0] = w[0];
-                    kw[t][1] = w[1];
-                }
-            }
-        }
         const __attribute__((address_space(3))) u32x4* op =
             (const __attribute__((address_space(3))) u32x4*)(spr + buf * SPR) + lane;
-        auto kop = [&](int t, int j) { return spread_int4_x16(kw[t][j]); };
         auto vop = [&](int c) { return op[c * 64]; };
         if (interior(s))
-            compute_with<false, true>(kop, vop, sc, s);
+            softmax_pv<false, true>(sa, sb, vop, sc, s);
         else
-            compute_with<false, false>(kop, vop, sc, s);
+            softmax_pv<false, false>(sa, sb, vop, sc, s);
     }
 
     // s_waitcnt vmcnt(N) lgkmcnt(0), then the workgroup barrier, as one statement the compiler
