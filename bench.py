@@ -722,6 +722,8 @@ def main():
     device = torch.device("cuda", 0)
     if args.workload == "append":
         rec = append_workload(device)
+        if args.copy_calibration:
+            rec["copy_calibration_GBps"] = copy_calibration(device)
         print(json.dumps({"metric": "INT4 KV append (rotation + quantization + pack) tokens/s",
                           "value": rec["tokens_per_s_b128"], "unit": "tokens/s", "n_gpus": 1, "steps": 512,
                           "warmup": 1, "ms_per_step": rec["append_step_us"]["b128"] * 1e-3, "higher_is_better": True,
