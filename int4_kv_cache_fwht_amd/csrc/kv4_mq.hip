@@ -197,10 +197,11 @@ struct MqWave {
     static constexpr int QOPS = NOPS / 4;          // operands a wave spreads
     static constexpr int NCOPY = 2 * CPB;          // copy instructions of a step
     static constexpr int PERW = (NCOPY + 3) / 4;   // copies a wave issues per step
-    static constexpr int SH_STAGES = 4;            // shared ring: steps s .. s + 3 (indices taken & 3)
+    static constexpr int SH_STAGES = 6;            // shared ring: steps k .. k + 5 of a pair iteration
     static constexpr int SH_RING = SH_STAGES * STAGE;
     static constexpr int SPR = NOPS * 64 * 16;     // one step's spread operands
-    static constexpr int SH_LDS = SH_RING + 2 * SPR;
+    static constexpr int SH_AREAS = 4;             // operand areas: steps k .. k + 3
+    static constexpr int SH_LDS = SH_RING + SH_AREAS * SPR;
     static_assert(NOPS % 4 == 0, "the operands split evenly over four waves");
 
     // One step's operands for this lane.  INT8 buffers hold twice the key and value bytes.
@@ -802,36 +803,49 @@ struct MqWave {
     }
     __device__ __forceinline__ static void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-    // One barrier per step, with the spread one step ahead of the products.  Before iteration i
-    // (step s = s0 + i) the ring holds steps s .. s + 2 (s + 1, s + 2 possibly in flight) and
-    // operand area i % 2 holds step s spread.  Iteration i: wait for this wave's copies of step
-    // s + 1; barrier (every copy of s + 1 has landed, area i % 2 is complete, and every wave is done
-    // with step s - 1: its stage and area (i + 1) % 2 are free); copy step s + 3 into the freed
-    // stage; spread this wave's quarter of step s + 1 into area (i + 1) % 2; compute step s.  Past
-    // s1 - 1 the copies repeat the last step and their spreads are never read.  [s0, s1) is the
-    // same for the four waves, so every wave passes the same barriers.
+    // Steps in pairs, one barrier per pair, with the spread one pair ahead of the products (the
+    // four waves then meet every other step, so a wave that runs late on one step can catch up on
+    // the next).  Before the iteration for steps k, k + 1 (offsets from s0) the ring holds steps
+    // k .. k + 3 (k + 2, k + 3 possibly in flight, the only copies in flight) and operand areas
+    // k % 4, (k + 1) % 4 hold steps k, k + 1 spread.  Iteration: wait for this wave's copies;
+    // barrier (every copy of k + 2, k + 3 has landed, both areas are complete, and every wave is
+    // done with steps k - 2, k - 1: their stages and areas are free); copy steps k + 4, k + 5 into
+    // the freed stages; spread this wave's quarter of steps k + 2, k + 3; compute steps k, k + 1.
+    // Past s1 - 1 the copies repeat the last step and their spreads are never read.  [s0, s1) is
+    // the same for the four waves, so every wave passes the same barriers.
     __device__ void run4_sh(int s0, int s1)
     {
         if (s0 >= s1) return;
-        uint32_t pa, pb;
+        const int n = s1 - s0;
+        uint32_t pa, pb, qa, qb;
 #pragma unroll
-        for (int j = 0; j < SH_STAGES - 1; j++) {
+        for (int j = 0; j < 4; j++) {
             step_pages(min(s0 + j, s1 - 1), pa, pb);
             stage_copy_sh(pa, pb, j);
         }
-        step_pages(min(s0 + SH_STAGES - 1, s1 - 1), pa, pb);
+        step_pages(min(s0 + 4, s1 - 1), pa, pb);
+        step_pages(min(s0 + 5, s1 - 1), qa, qb);
         __builtin_amdgcn_sched_barrier(0);
-        barrier_vm<(SH_STAGES - 2) * PERW>();
+        barrier_vm<2 * PERW>();
         __builtin_amdgcn_sched_barrier(0);
         spread_quarter(0, 0);
-        for (int i = 0; i < s1 - s0; i++) {
+        spread_quarter(1, 1);
+        int sk = 0; // k % SH_STAGES
+        for (int k = 0; k < n; k += 2) {
             __builtin_amdgcn_sched_barrier(0);
-            barrier_vm<(SH_STAGES - 3) * PERW>();
+            barrier_vm<0>();
             __builtin_amdgcn_sched_barrier(0);
-            stage_copy_sh(pa, pb, (i + 3) & 3);
-            step_pages(min(s0 + i + SH_STAGES, s1 - 1), pa, pb);
-            spread_quarter((i + 1) & 3, (i + 1) & 1);
-            compute_sh(i & 3, i & 1, s0 + i);
+            const int s4 = sk + 4 < SH_STAGES ? sk + 4 : sk + 4 - SH_STAGES;
+            const int s2 = sk + 2 < SH_STAGES ? sk + 2 : sk + 2 - SH_STAGES;
+            stage_copy_sh(pa, pb, s4);
+            stage_copy_sh(qa, qb, s4 + 1);
+            step_pages(min(s0 + k + 6, s1 - 1), pa, pb);
+            step_pages(min(s0 + k + 7, s1 - 1), qa, qb);
+            spread_quarter(s2, (k + 2) & 3);
+            spread_quarter(s2 + 1, (k + 3) & 3);
+            compute_sh(sk, k & 3, s0 + k);
+            if (k + 1 < n) compute_sh(sk + 1, (k + 1) & 3, s0 + k + 1);
+            sk = s2;
         }
         __builtin_amdgcn_sched_barrier(0);
         barrier_vm<0>();
