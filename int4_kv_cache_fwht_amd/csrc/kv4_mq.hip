@@ -775,9 +775,14 @@ struct MqWave {
 #pragma unroll
             for (int i = 0; i < 4; i++) sc[4 * j + i] = w[i];
         }
+        // the value operands are read here, ahead of the products and branches that precede
+        // their use, so that their LDS latency is covered
         const __attribute__((address_space(3))) u32x4* op =
             (const __attribute__((address_space(3))) u32x4*)(spr + buf * SPR) + lane;
-        auto vop = [&](int c) { return op[c * 64]; };
+        u32x4 vv[NCB];
+#pragma unroll
+        for (int c = 0; c < NCB; c++) vv[c] = op[c * 64];
+        auto vop = [&](int c) { return vv[c]; };
         if (interior(s))
             softmax_pv<false, true>(sa, sb, vop, sc, s);
         else
