@@ -794,19 +794,14 @@ struct MqWave {
     template <int N>
     __device__ __forceinline__ static void barrier_vm()
     {
-        static_assert(N >= 0 && N < 16, "small vmcnt");
+        static_assert(N == 0 || N == 2 || N == 4, "the counts the step loop uses");
         if constexpr (N == 0)
             asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        else if constexpr (N == 1)
-            asm volatile("s_waitcnt vmcnt(1) lgkmcnt(0)\n\ts_barrier" ::: "memory");
         else if constexpr (N == 2)
             asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        else if constexpr (N == 4)
-            asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
         else
-            static_assert(N <= 2 || N == 4, "add the count");
+            asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
-    __device__ __forceinline__ static void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
     // Steps in pairs, one barrier per pair, with the spread one pair ahead of the products (the
     // four waves then meet every other step, so a wave that runs late on one step can catch up on
