@@ -104,6 +104,26 @@ def test_mq_chunked_prefill():
     assert err <= TOL
 
 
+def test_mq_chunked_prefill_shared():
+    """A 256-position prefill chunk after 1000 cached positions: 64 row tiles per kv head, so the
+    workgroup-shared kernel runs; the same bits as the per-wave kernel, and the oracle's values."""
+    _print_case("mq_chunk_shared")
+    hq, hkv, d = 32, 8, 128
+    p = Pair(hq, hkv, d, num_pages=256, max_seqs=2, max_pps=128, S=4, R=128, b=128)
+    k, v = _kv(1256, hkv, d, seed=51)
+    p.append([1], [1000], k[:1000].contiguous(), v[:1000].contiguous())
+    p.append([1], [256], k[1000:].contiguous(), v[1000:].contiguous())
+    q = _q(256, hq, d, seed=52)
+    p.gpu.set_mq_share(False)
+    own = p.gpu.multi_query_attention([1], [256], q).cpu().numpy()
+    p.gpu.set_mq_share(True)
+    out, ref = p.multi([1], [256], q)
+    assert np.array_equal(out.astype(np.float32), own), "shared and per-wave steps differ"
+    err = np.abs(out - ref).max()
+    print("mq chunk (shared) max-abs", err)
+    assert err <= TOL
+
+
 def test_mq_full_size_sampled():
     """Qwen3-8B-shaped layer (64 sequences, lengths uniform in [1024, 8192]) with 4 query rows per
     sequence in one call; the oracle checks a sample of the sequences."""
