@@ -104,6 +104,31 @@ def test_mq_chunked_prefill():
     assert err <= TOL
 
 
+@pytest.mark.parametrize("seed", [101, 102, 103])
+def test_mq_shared_steps_random(seed):
+    """Seeded random calls for the workgroup-shared kernel: 5 sequences of random lengths, each with
+    16, 32, 48 or 64 query rows (G 4: 4 to 16 row tiles, a multiple of 4), in a random order."""
+    rng = np.random.default_rng(seed)
+    nqs = [int(x) for x in rng.choice([16, 32, 48, 64], size=5)]
+    lens = [int(rng.integers(nq, 3000)) for nq in nqs]
+    _print_case("mq_shared_random", seed=seed, lens=lens, nqs=nqs)
+    hq, hkv, d = 32, 8, 128
+    p = Pair(hq, hkv, d, num_pages=1024, max_seqs=8, max_pps=200, S=4, R=128, b=128)
+    _fill(p, lens, hkv, d, seed=seed)
+    q = _q(sum(nqs), hq, d, seed=seed + 1)
+    order = [int(i) for i in rng.permutation(5)]
+    qo = _reorder(q, nqs, order)
+    ids, nq = order, [nqs[i] for i in order]
+    p.gpu.set_mq_share(False)
+    own = p.gpu.multi_query_attention(ids, nq, qo).cpu().numpy()
+    p.gpu.set_mq_share(True)
+    out, ref = p.multi(ids, nq, qo)
+    assert np.array_equal(out.astype(np.float32), own), "shared and per-wave steps differ"
+    err = np.abs(out - ref).max()
+    print("mq shared random max-abs", err)
+    assert err <= TOL
+
+
 def test_mq_chunked_prefill_shared():
     """A 256-position prefill chunk after 1000 cached positions: 64 row tiles per kv head, so the
     workgroup-shared kernel runs; the same bits as the per-wave kernel, and the oracle's values."""
