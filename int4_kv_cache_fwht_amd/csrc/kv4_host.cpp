@@ -800,8 +800,18 @@ kv4_status kv4_multi_query_attention(kv4_cache_t h, int32_t n_seqs, const int32_
     }
     e = kv4::launch_mq_split(D, G, h->st.cfg.format, a, strm, t_split);
     if (e != hipSuccess) return hip_fail(h, e, "multi-query split launch");
-    e = kv4::launch_mq_merge(D, G, a, strm, t_merge);
-    if (e != hipSuccess) return hip_fail(h, e, "multi-query merge launch");
+    // row tiles of a single chunk are written by the split kernel; the merge runs for the others
+    bool merge = false;
+    for (const kv4::MqEntry& en : plan.entries) merge = merge || en.nch > 1;
+    if (merge) {
+        e = kv4::launch_mq_merge(D, G, a, strm, t_merge);
+        if (e != hipSuccess) return hip_fail(h, e, "multi-query merge launch");
+    } else if (h->prof.on) {
+        // no merge: its event pair brackets nothing
+        e = hipEventRecord(ev[2], strm);
+        if (e == hipSuccess) e = hipEventRecord(ev[3], strm);
+        if (e != hipSuccess) return hip_fail(h, e, "hipEventRecord");
+    }
     if (h->prof.on) h->prof.mq_ev.push_back(ev);
     return KV4_OK;
 }

@@ -851,12 +851,54 @@ struct MqWave {
         barrier_vm<0>();
     }
 
-    __device__ void finish(int task)
+    // The task's partial into slot `task`; or, when the row tile is one chunk (e.nch == 1), the
+    // output rows themselves: what the merge does with a single partial (divide by l, the inverse
+    // rotation, the scale fl32(1/sqrt(b))), with the stages across the lane's 16-lane row (dims
+    // 16 c + n: h < 16) and then across its column blocks (h >= 16).
+    __device__ void finish(int task, const MqEntry& e, int rt)
     {
         lsum += lane_xor16(lsum);
         lsum = add_xor32(lsum);
         zsum += lane_xor16(zsum);
         zsum = add_xor32(zsum);
+        if (e.nch == 1) {
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int row = 4 * g + i;
+                const float z = __shfl(zsum, row, 64);
+                const float inv = 1.f / (__shfl(lsum, row, 64) * (1.f / kPScale));
+                float x[NCB];
+#pragma unroll
+                for (int c = 0; c < NCB; c++) x[c] = ((acc[c][i] + z) * (1.f / kPScale)) * inv;
+                static_for<0, 4>([&](auto S) {
+                    constexpr int M = 1 << S;
+                    if (M < a.block) {
+                        const float sgn = (lane & M) ? -1.f : 1.f;
+#pragma unroll
+                        for (int c = 0; c < NCB; c++) x[c] = butterfly_xor<M>(x[c], sgn);
+                    }
+                });
+#pragma unroll
+                for (int hc = 1; hc < NCB; hc <<= 1) {
+                    if (16 * hc < a.block) {
+#pragma unroll
+                        for (int c = 0; c < NCB; c++) {
+                            if (c & hc) continue;
+                            const float u = x[c], w = x[c + hc];
+                            x[c] = u + w;
+                            x[c + hc] = u - w;
+                        }
+                    }
+                }
+                const int jq = rt * QT + row / G, gi = row % G;
+                if (jq < e.nq) {
+                    float* out = a.out + ((int64_t)(e.qrow0 + jq) * a.hq + head * G + gi) * D + n;
+#pragma unroll
+                    for (int c = 0; c < NCB; c++) out[16 * c] = x[c] * a.cb;
+                }
+            }
+            return;
+        }
         if (g == 0) {
             float* ml = a.part_ml + ((int64_t)task * kMqRows + n) * 2;
             ml[0] = m_ref;
@@ -944,7 +986,7 @@ __device__ __forceinline__ void mq_split_task(const MqArgs& a, int wave, int lan
         else
             W.run4(s0 > n8 ? s0 : n8, s1);
     }
-    W.finish(wave);
+    W.finish(wave, e, rt);
 }
 
 template <int D, int G, int FMT>
@@ -996,6 +1038,7 @@ __global__ __launch_bounds__(256) void mq_merge_kernel(MqArgs a)
     const int task0 = mq_uniform(&a.entries[lo].task0);
     const int grp0 = mq_uniform(&a.entries[lo].grp0);
     const int nch = mq_uniform(&a.entries[lo].nch);
+    if (nch == 1) return; // the split kernel wrote these rows from their single partial
     const int nrt = (nq * G + kMqRows - 1) / kMqRows;
     const int local = grp - grp0;
     const int head = local / nrt, rt = local - head * nrt;
