@@ -156,7 +156,6 @@ __device__ __forceinline__ float hi_half(uint32_t d) { return (float)__builtin_b
 
 __device__ __forceinline__ u32x4 ld16(const uint8_t* p) { return *(const u32x4*)p; }
 __device__ __forceinline__ u32x2 ld8(const uint8_t* p) { return *(const u32x2*)p; }
-__device__ __forceinline__ uint32_t ld4(const uint8_t* p) { return *(const uint32_t*)p; }
 
 // The call entry that holds `key`: the last entry whose first task (GRP false) or first merge
 // group (GRP true) is <= key (both increase along the entries).  Lane l reads entry l of each round
