@@ -180,3 +180,63 @@ def test_multi_plan_errors(driver):
         assert _plan(pl, 100, [(0, 1)])[0]["status"] == 5    # BF16: unsupported
     finally:
         pl.close()
+
+
+def _xcd_grouped_block(b, nb):
+    """Workgroup b's task block (kv4_mq.hip: xcd_grouped_block())."""
+    full = nb // 32 * 32
+    if b >= full:
+        return b
+    xcd, slot = b & 7, b >> 3
+    return (slot >> 2) * 32 + xcd * 4 + (slot & 3)
+
+
+@pytest.mark.parametrize("nb", [1, 5, 31, 32, 33, 64, 95, 257, 1024])
+def test_xcd_grouped_block_is_a_bijection(nb):
+    got = [_xcd_grouped_block(b, nb) for b in range(nb)]
+    assert sorted(got) == list(range(nb))
+    full = nb // 32 * 32
+    for b in range(full):
+        # four consecutive task blocks run on one XCD (b % 8)
+        assert _xcd_grouped_block(b, nb) // 4 == (b >> 5) * 8 + (b & 7)
+
+
+@pytest.mark.parametrize("lens,nqs,target", [
+    ([300, 700, 2000, 5000], [16, 13, 64, 61], 64),
+    ([300, 700, 2000, 5000], [16, 13, 64, 61], 4096),
+    ([4096] * 6, [64] * 6, 100000),
+    ([1000 + 256], [256], 512),
+])
+def test_shared_workgroups_take_four_row_tiles_of_one_chunk(driver, lens, nqs, target):
+    """The workgroup-shared multi-query kernel is launched when every entry has a multiple of 4
+    row tiles; its four waves (tasks 4k .. 4k + 3) must then be row tiles of one (entry, kv head,
+    chunk), so that they stage the same pages and pass the same barriers."""
+    hq, hkv = 32, 8
+    G = hq // hkv
+    pl = Planner(driver)
+    try:
+        first, _ = pl.cmd("init %d %d 128 16 8192 16 512 4 128 128 0" % (hq, hkv))
+        assert first == ["status", "0"]
+        for i, L in enumerate(lens):
+            assert pl.cmd("append 1 %d %d" % (i, L), block=True)[0] == ["status", "0"]
+        st, entries = _plan(pl, target, list(enumerate(nqs)))
+        assert st["status"] == 0
+        assert all(-(-int(e[2]) * G // 16) % 4 == 0 for e in entries)
+        assert st["tasks"] % 4 == 0
+        task0s = [int(e[4]) for e in entries]
+        where = []
+        for w in range(st["tasks"]):
+            ei = max(i for i, t0 in enumerate(task0s) if t0 <= w)
+            nq, nch = int(entries[ei][2]), int(entries[ei][7])
+            nrt = -(-nq * G // 16)
+            local = w - task0s[ei]
+            head = local // (nch * nrt)
+            local -= head * nch * nrt
+            chunk, rt = divmod(local, nrt)
+            where.append((ei, head, chunk, rt))
+        for k in range(0, st["tasks"], 4):
+            quad = where[k:k + 4]
+            assert len({q[:3] for q in quad}) == 1, quad
+            assert [q[3] for q in quad] == list(range(quad[0][3], quad[0][3] + 4)), quad
+    finally:
+        pl.close()
