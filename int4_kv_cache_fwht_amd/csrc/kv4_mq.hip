@@ -222,7 +222,7 @@ struct MqWave {
     const uint8_t* hbase; // the pool at this kv head's block of page 0
     uint32_t pstride;     // bytes from one page to the next (all kv heads' blocks)
     int p0, p1;          // INT4 page range (INT4_PROT) or page count (INT8 format: p1)
-    float m_ref = -__builtin_inff(), lsum = 0.f, zsum = 0.f, Ar = 0.f, Br = 0.f;
+    float m_ref = -__builtin_inff(), lsum = 0.f, zsum = 0.f, Ar = 0.f, Bu = 0.f;
     __attribute__((address_space(3))) uint8_t* ring; // kMqStages INT4 stage buffers (the wave's or the workgroup's)
     __attribute__((address_space(3))) uint8_t* spr;  // shared steps: the spread operands [NOPS][64 lanes][16 B]
     int wv = 0;          // shared steps: wave index in the workgroup
@@ -298,9 +298,10 @@ struct MqWave {
             for (int i = 0; i < 8; i++) y[i] = __builtin_ldexpf(x[8 * j + i], 14 - E - ((i & 1) ? 4 : 0));
             split_hilo(y, qhi[j], qlo[j]);
         }
-        // score (log2 units) = Ar * s_K * acc + Br * z_K, acc = 2^-24 sum(q 2^(14-E) * code)
+        // score (log2 units) = Ar * (s_K * acc + Bu * z_K), acc = 2^-24 sum(q 2^(14-E) * code):
+        // a step keeps the bracket (st) and applies Ar once per position, in the exponent's fma
         Ar = __builtin_ldexpf(a.scale_log2, 24 + E - 14);
-        Br = a.scale_log2 * sum;
+        Bu = __builtin_ldexpf(sum, 14 - 24 - E);
 #pragma unroll
         for (int c = 0; c < NCB; c++) acc[c] = (float4_t){0.f, 0.f, 0.f, 0.f};
     }
@@ -483,8 +484,8 @@ struct MqWave {
         }
         // fp16 scales enter the fp32 arithmetic as fma operands (v_fma_mix_f32: no conversions).
         // The reference bound uses one exponent per lane: the largest s_V of the lane's readable
-        // positions (positive fp16 patterns order like their values), so st + e_lane bounds
-        // st + log2 s_V + 1 for each of them.
+        // positions (positive fp16 patterns order like their values), so Ar st + e_lane bounds
+        // Ar st + log2 s_V + 1 for each of them (Ar > 0: the largest st gives the largest score).
         float st[8];
         bool ok[8];
         float smax = -__builtin_inff();
@@ -493,7 +494,7 @@ struct MqWave {
         for (int t = 0; t < 8; t++) {
             const float r = t < 4 ? sa[t] : sb[t - 4];
             const uint32_t d0 = b.sc[2 * t], d1 = b.sc[2 * t + 1];
-            st[t] = fmaf(lo_half(d0), r * Ar, fmaf(hi_half(d0), Br, 0.f));
+            st[t] = fmaf(lo_half(d0), r, fmaf(hi_half(d0), Bu, 0.f));
             ok[t] = FULL || pos[t] <= pos_r;
             smax = ok[t] ? fmaxf(smax, st[t]) : smax;
             if (!FULL) svmax = ok[t] ? max(svmax, d1 & 0xFFFFu) : svmax;
@@ -505,7 +506,7 @@ struct MqWave {
             for (int t = 1; t < 8; t++) mv = __builtin_elementwise_max(mv, as_u16x2(b.sc[2 * t + 1]));
             svmax = mv.x;
         }
-        float wmax = smax + (float)(svmax >> 10);
+        float wmax = fmaf(smax, Ar, (float)(svmax >> 10));
         wmax = fmaxf(wmax, lane_xor16(wmax));
         wmax = max_xor32(wmax);
         const bool need = wmax > m_ref + kMqTau;
@@ -530,7 +531,7 @@ struct MqWave {
             const uint32_t d1 = b.sc[2 * t + 1];
             // unread slots hold unspecified bytes (their scales may be inf / NaN): select, never
             // multiply them by zero
-            const float p = ok[t] ? __builtin_amdgcn_exp2f(st[t] - m27) : 0.f;
+            const float p = ok[t] ? __builtin_amdgcn_exp2f(fmaf(st[t], Ar, -m27)) : 0.f;
             lsum += p;
             zsum = ok[t] ? fmaf(p, fmaf(lo_half(d1), (float)MID, hi_half(d1)), zsum) : zsum;
             P[t] = ok[t] ? fmaf(lo_half(d1), p, 0.f) : 0.f;
@@ -576,8 +577,8 @@ struct MqWave {
         if (!FULL) positions<IS8>(s, pos);
         // fp16 scales enter the fp32 arithmetic as fma operands (v_fma_mix_f32: no conversions).
         // The reference bound uses one exponent per lane: the largest s_V of the lane's readable
-        // positions (positive fp16 patterns order like their values), so st + e_lane bounds
-        // st + log2 s_V + 1 for each of them.
+        // positions (positive fp16 patterns order like their values), so Ar st + e_lane bounds
+        // Ar st + log2 s_V + 1 for each of them (Ar > 0: the largest st gives the largest score).
         float st[8];
         bool ok[8];
         float smax = -__builtin_inff();
@@ -586,7 +587,7 @@ struct MqWave {
         for (int t = 0; t < 8; t++) {
             const float r = t < 4 ? sa[t] : sb[t - 4];
             const uint32_t d0 = sc[2 * t], d1 = sc[2 * t + 1];
-            st[t] = fmaf(lo_half(d0), r * Ar, fmaf(hi_half(d0), Br, 0.f));
+            st[t] = fmaf(lo_half(d0), r, fmaf(hi_half(d0), Bu, 0.f));
             ok[t] = FULL || pos[t] <= pos_r;
             smax = ok[t] ? fmaxf(smax, st[t]) : smax;
             if (!FULL) svmax = ok[t] ? max(svmax, d1 & 0xFFFFu) : svmax;
@@ -598,7 +599,7 @@ struct MqWave {
             for (int t = 1; t < 8; t++) mv = __builtin_elementwise_max(mv, as_u16x2(sc[2 * t + 1]));
             svmax = mv.x;
         }
-        float wmax = smax + (float)(svmax >> 10);
+        float wmax = fmaf(smax, Ar, (float)(svmax >> 10));
         wmax = fmaxf(wmax, lane_xor16(wmax));
         wmax = max_xor32(wmax);
         const bool need = wmax > m_ref + kMqTau;
@@ -623,7 +624,7 @@ struct MqWave {
             const uint32_t d1 = sc[2 * t + 1];
             // unread slots hold unspecified bytes (their scales may be inf / NaN): select, never
             // multiply them by zero
-            const float p = ok[t] ? __builtin_amdgcn_exp2f(st[t] - m27) : 0.f;
+            const float p = ok[t] ? __builtin_amdgcn_exp2f(fmaf(st[t], Ar, -m27)) : 0.f;
             lsum += p;
             zsum = ok[t] ? fmaf(p, fmaf(lo_half(d1), (float)MID, hi_half(d1)), zsum) : zsum;
             P[t] = ok[t] ? fmaf(lo_half(d1), p, 0.f) : 0.f;
