@@ -95,18 +95,27 @@ __device__ __forceinline__ u32x4 centre(u32x4 x)
     return r;
 }
 
-// Eight INT4 value codes in the spread order, centred: (nibble | 0x6400) is the fp16 value
-// 1024 + code, less 1024 + MID in one packed fp16 subtraction.  k6400 holds 0x64006400 in a
-// vector register, so that mask-and-or is one v_and_or_b32 (two literals cannot share it).
+// Eight INT4 value codes in the spread order, centred.  A nibble in bits 0-3 of a half,
+// or'ed with 0x6400, is the fp16 value 1024 + code, less 1024 + MID in one packed fp16
+// subtraction; a nibble left in bits 4-7 gives 1024 + 16 code, and (1024 + 16 code) / 16 - 64 - MID
+// is one packed fp16 fma.  Both are exact (integers below 2^11), so one shift serves four
+// codes.  k6400 holds 0x64006400 in a vector register, so that mask-and-or is one v_and_or_b32
+// (two literals cannot share it).
 template <int MID>
 __device__ __forceinline__ u32x4 spread_centre_int4(uint32_t w, uint32_t k6400)
 {
     const half2_t off = {(_Float16)(-(1024 + MID)), (_Float16)(-(1024 + MID))};
-    u32x4 r;
-#pragma unroll
-    for (int s = 0; s < 4; s++)
-        r[s] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, ((w >> (4 * s)) & 0x000F000Fu) | k6400) + off);
-    return r;
+    const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+    const half2_t off16 = {(_Float16)(-(64 + MID)), (_Float16)(-(64 + MID))};
+    const uint32_t w8 = w >> 8;
+    const half2_t e0 = __builtin_bit_cast(half2_t, (w & 0x000F000Fu) | k6400);
+    const half2_t o0 = __builtin_bit_cast(half2_t, (w & 0x00F000F0u) | k6400);
+    const half2_t e1 = __builtin_bit_cast(half2_t, (w8 & 0x000F000Fu) | k6400);
+    const half2_t o1 = __builtin_bit_cast(half2_t, (w8 & 0x00F000F0u) | k6400);
+    return (u32x4){__builtin_bit_cast(uint32_t, e0 + off),
+                   __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(o0, sixteenth, off16)),
+                   __builtin_bit_cast(uint32_t, e1 + off),
+                   __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(o1, sixteenth, off16))};
 }
 
 // A pair of fp16 values times 16 (exact: the values stay below 2^14).
